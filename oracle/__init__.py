@@ -1,0 +1,6 @@
+"""The float64 CPU oracle: test infrastructure, never part of the product path.
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.
+"""
+from .attention import attention_ref, attention_rows_ref  # noqa: F401

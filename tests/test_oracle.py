@@ -1,0 +1,334 @@
+"""Pins for the float64 oracle against what the pages and the mathematics fix.
+
+None of these checks retypes the oracle's formula: each one compares it with a
+closed form (T=1, T=2, constant scores), an invariant (causality, row shift,
+linearity, GQA replication, weights summing to one), a brute-force
+high-precision evaluation on tiny inputs, an independent library routine
+(torch's scaled-dot-product attention and logsumexp), or the constant that the
+Graph page prints.  The last test plants plausible mistakes in a copy of the
+oracle and checks that these pins catch every one of them.
+"""
+import inspect
+import json
+import math
+import os
+import struct
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from causal_attention_forward_amd.inputs import SCALE_C, WORKLOADS, make_inputs, make_workload
+from oracle import attention as oracle_mod
+from oracle import attention_ref, attention_rows_ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+C = float(SCALE_C)
+
+
+def bits32(x):
+    return struct.unpack("<I", struct.pack("<f", float(np.float32(x))))[0]
+
+
+def from_bits32(b):
+    return struct.unpack("<f", struct.pack("<I", b))[0]
+
+
+# --------------------------------------------------------------------------
+# the constant c (Graph page: cgScoreScale, cgStreamingScale)
+# --------------------------------------------------------------------------
+def test_scale_constant_matches_pages():
+    g = json.load(open(os.path.join(GOLDEN, "streaming_scale.json")))
+    # the score scale the page pins is the binary32 nearest 1/sqrt(64)
+    assert bits32(1.0 / math.sqrt(g["head_width"])) == g["score_scale_bits"]
+    # c = bits(binary32 log2 e) minus three exponent steps
+    c_bits = bits32(math.log2(math.e)) - g["exponent_steps_subtracted"] * g["exponent_step"]
+    assert c_bits == 0x3E38AA3B
+    assert bits32(SCALE_C) == c_bits
+    # ... which is exactly the binary32 nearest scale / ln 2
+    assert bits32(0.125 / math.log(2.0)) == c_bits
+    assert abs(from_bits32(c_bits) * math.log(2.0) - 0.125) < 2e-9
+
+
+# --------------------------------------------------------------------------
+# pins, written so they can also be run against a mutated oracle
+# --------------------------------------------------------------------------
+def pin_T1(ref):
+    """T=1: O_0 = V_0 exactly and L_0 = t_00 = c (q_0 . k_0)."""
+    x = make_inputs(1, 6, 3, seed=11)
+    O, L = ref(x.Q, x.K, x.Vt, x.c)
+    for h in range(6):
+        kv = h // 2
+        v0 = x.Vt[kv, :, 0].astype(np.float64)
+        if not np.array_equal(O[0, h * 64:(h + 1) * 64], v0):
+            return False
+        t00 = C * float(np.dot(x.Q[h, 0].astype(np.float64), x.K[kv, 0].astype(np.float64)))
+        if not abs(L[h, 0] - t00) <= 1e-12 * max(1.0, abs(t00)):
+            return False
+    return True
+
+
+def pin_constant_scores(ref):
+    """Q = 0: every visible score equals 0, so O_i is the prefix mean of V and
+    L_i = log2(i + 1).  T=200 crosses several 64-row tiles and a ragged tail."""
+    x = make_inputs(200, 4, 2, seed=12)
+    Q = np.zeros_like(x.Q)
+    O, L = ref(Q, x.K, x.Vt, x.c)
+    ok = True
+    for h in range(4):
+        V = x.Vt[h // 2].astype(np.float64).T
+        prefix = np.cumsum(V, axis=0) / np.arange(1, 201)[:, None]
+        ok &= np.allclose(O[:, h * 64:(h + 1) * 64], prefix, rtol=0, atol=1e-12)
+        ok &= np.allclose(L[h], np.log2(np.arange(1, 201)), rtol=0, atol=1e-12)
+    return bool(ok)
+
+
+def pin_equal_keys(ref):
+    """All K rows equal: scores of a row are all equal (nonzero here), so again
+    the prefix mean, and L_i = t_i + log2(i + 1)."""
+    x = make_inputs(70, 1, 1, seed=13)
+    K = np.repeat(x.K[:, :1, :], 70, axis=1)
+    O, L = ref(x.Q, K, x.Vt, x.c)
+    V = x.Vt[0].astype(np.float64).T
+    prefix = np.cumsum(V, axis=0) / np.arange(1, 71)[:, None]
+    t = C * (x.Q[0].astype(np.float64) @ K[0, 0].astype(np.float64))
+    return bool(np.allclose(O, prefix, rtol=0, atol=1e-12)
+                and np.allclose(L[0], t + np.log2(np.arange(1, 71)), rtol=0, atol=1e-12))
+
+
+def pin_T2(ref):
+    """T=2: O_1 = (2^t10 V_0 + 2^t11 V_1) / (2^t10 + 2^t11)."""
+    x = make_inputs(2, 2, 1, seed=14)
+    O, L = ref(x.Q, x.K, x.Vt, x.c)
+    V = x.Vt[0].astype(np.float64).T
+    for h in range(2):
+        q = x.Q[h, 1].astype(np.float64)
+        t0 = C * float(q @ x.K[0, 0].astype(np.float64))
+        t1 = C * float(q @ x.K[0, 1].astype(np.float64))
+        a, b = 2.0 ** t0, 2.0 ** t1
+        want = (a * V[0] + b * V[1]) / (a + b)
+        if not np.allclose(O[1, h * 64:(h + 1) * 64], want, rtol=0, atol=1e-12):
+            return False
+        if abs(L[h, 1] - math.log2(a + b)) > 1e-12:
+            return False
+    return True
+
+
+def pin_weights_sum_to_one(ref):
+    """V = 1 everywhere: each row's softmax weights sum to 1, so O = 1."""
+    x = make_inputs(150, 2, 2, seed=15)
+    O, _ = ref(x.Q, x.K, np.ones_like(x.Vt), x.c)
+    return bool(np.allclose(O, 1.0, rtol=0, atol=1e-12))
+
+
+def _decimal_row(Q, K, Vt, c, h, i, G):
+    """One output row by exact rational scores and 40-digit exponentials."""
+    getcontext().prec = 40
+    kv = h // G
+    ln2 = Decimal(2).ln()
+    cf = Fraction(float(c))
+    ts = []
+    for j in range(i + 1):
+        s = sum(Fraction(float(Q[h, i, d])) * Fraction(float(K[kv, j, d])) for d in range(64))
+        t = s * cf
+        ts.append(Decimal(t.numerator) / Decimal(t.denominator))
+    ws = [(t * ln2).exp() for t in ts]
+    Z = sum(ws)
+    o = [sum(ws[j] * Decimal(float(Vt[kv, d, j])) for j in range(i + 1)) / Z for d in range(64)]
+    L = Z.ln() / ln2
+    return np.array([float(v) for v in o]), float(L)
+
+
+def pin_brute_force(ref):
+    """Every element of a T=7, Hq=4, Hkv=2 case against exact rational scores
+    and 40-digit exponentials, computed element by element."""
+    x = make_inputs(7, 4, 2, seed=16, qk_std=1.5)
+    O, L = ref(x.Q, x.K, x.Vt, x.c)
+    for h in range(4):
+        for i in range(7):
+            o, l = _decimal_row(x.Q, x.K, x.Vt, x.c, h, i, 2)
+            if not np.allclose(O[i, h * 64:(h + 1) * 64], o, rtol=0, atol=1e-12):
+                return False
+            if abs(L[h, i] - l) > 1e-12:
+                return False
+    return True
+
+
+def _torch_reference(x):
+    import torch
+    G = x.Hq // x.Hkv
+    q = torch.from_numpy(x.Q.astype(np.float64))
+    k = torch.from_numpy(x.K.astype(np.float64)).repeat_interleave(G, dim=0)
+    v = torch.from_numpy(x.Vt.astype(np.float64)).transpose(1, 2).repeat_interleave(G, dim=0)
+    scale = float(x.c) * math.log(2.0)  # natural-log scale equivalent to base-2 c
+    o = torch.nn.functional.scaled_dot_product_attention(
+        q[None], k[None], v[None], is_causal=True, scale=scale)[0]     # [Hq][T][64]
+    O = o.permute(1, 0, 2).reshape(x.T, x.Hq * 64).numpy()
+    s = torch.matmul(q, k.transpose(1, 2)) * scale
+    mask = torch.ones(x.T, x.T, dtype=torch.bool).triu(1)
+    s = s.masked_fill(mask, float("-inf"))
+    L = (torch.logsumexp(s, dim=-1) / math.log(2.0)).numpy()
+    return O, L
+
+
+def pin_library(ref):
+    """torch's scaled-dot-product attention (causal, float64, CPU) with K/V
+    repeated per query group, and torch.logsumexp for L, on a ragged GQA case."""
+    x = make_inputs(333, 6, 2, seed=17, peaked_fraction=0.02)
+    O, L = ref(x.Q, x.K, x.Vt, x.c)
+    Ot, Lt = _torch_reference(x)
+    return bool(np.allclose(O, Ot, rtol=0, atol=1e-10) and np.allclose(L, Lt, rtol=0, atol=1e-10))
+
+
+def pin_causality(ref):
+    """Changing keys and values after row i0 leaves rows 0..i0 unchanged."""
+    x = make_inputs(130, 2, 1, seed=18)
+    O1, L1 = ref(x.Q, x.K, x.Vt, x.c)
+    rng = np.random.default_rng(99)
+    K2, Vt2 = x.K.copy(), x.Vt.copy()
+    i0 = 77
+    K2[:, i0 + 1:] = rng.standard_normal(K2[:, i0 + 1:].shape).astype(np.float16)
+    Vt2[:, :, i0 + 1:] = rng.standard_normal(Vt2[:, :, i0 + 1:].shape).astype(np.float16)
+    O2, L2 = ref(x.Q, K2, Vt2, x.c)
+    same = np.array_equal(O1[:i0 + 1], O2[:i0 + 1]) and np.array_equal(L1[:, :i0 + 1], L2[:, :i0 + 1])
+    changed = not np.allclose(O1[i0 + 1:], O2[i0 + 1:])
+    return bool(same and changed)
+
+
+def pin_row_shift(ref):
+    """Adding one vector u to every K row leaves O unchanged and shifts L_i by
+    c (q_i . u).  K is put on a 1/64 grid and u on a 1/4 grid so that K + u is
+    still exact in fp16."""
+    x = make_inputs(100, 2, 1, seed=19)
+    K1 = (np.round(x.K.astype(np.float64) * 64) / 64).astype(np.float16)   # 1/64 grid
+    u = (np.arange(64) % 5 - 2).astype(np.float64) * 0.25
+    K2 = (K1.astype(np.float64) + u).astype(np.float16)
+    if not np.array_equal(K2.astype(np.float64), K1.astype(np.float64) + u):
+        return False
+    O1, L1 = ref(x.Q, K1, x.Vt, x.c)
+    O2, L2 = ref(x.Q, K2, x.Vt, x.c)
+    shift = C * (x.Q.astype(np.float64) @ u)                       # [Hq][T]
+    return bool(np.allclose(O1, O2, rtol=0, atol=1e-11) and np.allclose(L2 - L1, shift, rtol=0, atol=1e-11))
+
+
+def pin_linearity(ref):
+    """O is linear in V for fixed Q, K; L does not depend on V."""
+    a = make_inputs(90, 2, 2, seed=20)
+    b = make_inputs(90, 2, 2, seed=21)
+    O1, L1 = ref(a.Q, a.K, a.Vt, a.c)
+    O2, _ = ref(a.Q, a.K, b.Vt, a.c)
+    Vs = (a.Vt.astype(np.float64) * 0.5 - b.Vt.astype(np.float64) * 2.0)
+    O3, L3 = ref(a.Q, a.K, Vs, a.c)
+    return bool(np.allclose(O3, 0.5 * O1 - 2.0 * O2, rtol=0, atol=1e-11) and np.array_equal(L1, L3))
+
+
+def pin_gqa_replication(ref):
+    """With Hkv heads, query head h reads K/V head h // G: the same result as
+    Hkv' = Hq after repeating each K/V head G times (repeat_interleave)."""
+    x = make_inputs(96, 6, 2, seed=22)
+    O1, L1 = ref(x.Q, x.K, x.Vt, x.c)
+    K6 = np.repeat(x.K, 3, axis=0)
+    V6 = np.repeat(x.Vt, 3, axis=0)
+    O2, L2 = ref(x.Q, K6, V6, x.c)
+    return bool(np.array_equal(O1, O2) and np.array_equal(L1, L2))
+
+
+def pin_token_major_layout(ref):
+    """O is [T][Hq*64]: head h's output occupies columns h*64..h*64+63 of each
+    token row, equal to a one-head call on that head alone."""
+    x = make_inputs(65, 3, 3, seed=23)
+    O, L = ref(x.Q, x.K, x.Vt, x.c)
+    for h in range(3):
+        Oh, Lh = ref(x.Q[h:h + 1], x.K[h:h + 1], x.Vt[h:h + 1], x.c)
+        if not (np.array_equal(O[:, h * 64:(h + 1) * 64], Oh) and np.array_equal(L[h], Lh[0])):
+            return False
+    return True
+
+
+PINS = [pin_T1, pin_constant_scores, pin_equal_keys, pin_T2, pin_weights_sum_to_one,
+        pin_brute_force, pin_library, pin_causality, pin_row_shift, pin_linearity,
+        pin_gqa_replication, pin_token_major_layout]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_oracle_pin(pin):
+    assert pin(attention_ref)
+
+
+def test_rows_ref_agrees_with_full():
+    x = make_inputs(300, 4, 2, seed=24, qk_std=1.5)
+    O, L = attention_ref(x.Q, x.K, x.Vt, x.c)
+    for h in (0, 3):
+        rows = [0, 1, 63, 64, 200, 299]
+        Or, Lr = attention_rows_ref(x.Q, x.K, x.Vt, x.c, h, rows)
+        assert np.allclose(Or, O[rows, h * 64:(h + 1) * 64], rtol=0, atol=1e-12)
+        assert np.allclose(Lr, L[h, rows], rtol=0, atol=1e-12)
+
+
+def test_rows_ref_brute_force():
+    x = make_inputs(6, 2, 1, seed=25)
+    Or, Lr = attention_rows_ref(x.Q, x.K, x.Vt, x.c, 1, range(6))
+    for i in range(6):
+        o, l = _decimal_row(x.Q, x.K, x.Vt, x.c, 1, i, 2)
+        assert np.allclose(Or[i], o, rtol=0, atol=1e-12)
+        assert abs(Lr[i] - l) <= 1e-12
+
+
+# --------------------------------------------------------------------------
+# planted mistakes: each mutant of the oracle must fail at least one pin
+# --------------------------------------------------------------------------
+MUTANTS = {
+    "diagonal dropped": ("t[cols > rows] = -np.inf", "t[cols >= rows] = -np.inf"),
+    "mask off by one": ("t[cols > rows] = -np.inf", "t[cols > rows + 1] = -np.inf"),
+    "no causal mask": ("t[cols > rows] = -np.inf", "pass"),
+    "head map h % Hkv": ("kv = h // G", "kv = h % Hkv"),
+    "scale dropped": ("* c        # base-2", "* 1.0      # base-2"),
+    "natural exponent": ("w = np.exp2(t - M)", "w = np.exp(t - M)"),
+    "natural-log L": ("(M + np.log2(Z))", "(M + np.log(Z))"),
+    "L without max": ("(M + np.log2(Z))", "(np.log2(Z))"),
+    "V untransposed": ("v = Vt[kv].astype(np.float64).T", "v = Vt[kv].astype(np.float64)"),
+    "no normalisation": ("(w @ v[:i1]) / Z", "(w @ v[:i1])"),
+    "K for Q": ("q = Q[h].astype(np.float64)", "q = K[kv].astype(np.float64)"),
+}
+
+
+def _mutant(old, new):
+    src = inspect.getsource(oracle_mod.attention_ref)
+    assert src.count(old) == 1, old
+    ns = dict(vars(oracle_mod))
+    exec(src.replace(old, new), ns)
+    return ns["attention_ref"]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name):
+    ref = _mutant(*MUTANTS[name])
+    caught = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                ok = pin(ref)
+        except Exception:
+            ok = False
+        if not ok:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the mutant '{name}'"
+
+
+# --------------------------------------------------------------------------
+# the input generator (host logic)
+# --------------------------------------------------------------------------
+def test_inputs_recipe():
+    x = make_workload(2)
+    w = WORKLOADS[2]
+    assert x.Q.shape == (16, 1000, 64) and x.K.shape == (4, 1000, 64) and x.Vt.shape == (4, 64, 1000)
+    assert x.Q.dtype == np.float16 and x.Vt.flags["C_CONTIGUOUS"]
+    y = make_workload(2)
+    assert np.array_equal(x.Q, y.Q) and np.array_equal(x.K, y.K) and np.array_equal(x.Vt, y.Vt)
+    # ten peaked key rows per K/V head: their mean is shifted by about +3
+    means = x.K.astype(np.float64).mean(axis=2)
+    for kv in range(4):
+        assert (means[kv] > 2.0).sum() == math.ceil(w.peaked_fraction * w.T)
+    z = make_workload(4)
+    assert 1.4 < z.Q.astype(np.float64).std() < 1.6 and 0.95 < z.Vt.astype(np.float64).std() < 1.05
