@@ -1,0 +1,151 @@
+"""Benchmark of the causal streaming-attention forward on one MI355X.
+
+One step = one sattn_fwd call over the T=4096, Hq=32, Hkv=8, d=64 workload
+(seeded synthetic fp16 inputs, already resident in HBM).  Prints one JSON
+line: causal TFLOP/s (4*T^2*64*Hq/2 flop per call), the roofline of the
+kernel against the fp16 dense MFMA peak, and the float64 CPU oracle timed on
+a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP16_TFLOPS = 2516.6  # MI355X dense fp16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk ("2.5 PF")
+WORKLOAD_INDEX = 3
+KERNEL_SRC = os.path.join(ROOT, "causal_attention_forward_amd", "csrc", "sattn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sattn_fwd_T4096_Hq32_Hkv8.txt")
+
+
+def causal_flops(T, Hq, d=64):
+    return 4.0 * T * T * d * Hq / 2.0
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_sha") != kernel_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(x, budget_s=20.0):
+    """The float64 oracle on whole heads of the same workload, as many as fit
+    in about budget_s seconds (at least one), scaled to TFLOP/s."""
+    from oracle import attention_ref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    t0 = time.perf_counter()
+    heads = 0
+    while heads < x.Hq:
+        attention_ref(x.Q, x.K, x.Vt, x.c, heads=[heads])
+        heads += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = causal_flops(x.T, 1) * heads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{heads} of {x.Hq} query heads of T={x.T} Hq={x.Hq} Hkv={x.Hkv} "
+                      f"({dt:.1f} s, float64 NumPy)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from causal_attention_forward_amd import sattn
+    from causal_attention_forward_amd.inputs import WORKLOADS, make_workload
+
+    w = WORKLOADS[WORKLOAD_INDEX]
+    x = make_workload(WORKLOAD_INDEX)
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(x.Q).to(dev)
+    k = torch.from_numpy(x.K).to(dev)
+    vt = torch.from_numpy(x.Vt).to(dev)
+    O = torch.empty((x.T, x.Hq * 64), dtype=torch.float16, device=dev)
+    L = torch.empty((x.Hq, x.T), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        sattn.fwd(q, k, vt, x.c, out=O, lse=L, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps  # average launch duration on the stream
+
+    flops = causal_flops(x.T, x.Hq)
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    traffic = measured_traffic()
+    out = {
+        "metric": "causal attn fwd TFLOP/s and % fp16 MFMA peak, T=4096 Hq=32 Hkv=8 d=64",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": x.T, "Hq": x.Hq, "Hkv": x.Hkv, "head_dim": 64,
+                   "causal": True, "flop_per_call": flops, "pct_fp16_peak": round(100 * value / PEAK_FP16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+                     "traffic": traffic, "kernel_ms": round(kernel_ms, 5)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
