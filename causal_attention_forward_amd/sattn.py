@@ -11,6 +11,12 @@ from __future__ import annotations
 import ctypes
 import os
 
+# torch owns the device memory and streams handed to the library, so its HIP
+# runtime must be the one libsattn binds to.  torch ships its own
+# libamdhip64; importing torch first makes the loader resolve libsattn's
+# dependency to that already-loaded runtime instead of mapping a second one.
+import torch  # noqa: E402,F401
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsattn.so")
 
@@ -18,6 +24,20 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
 
 _lib = ctypes.CDLL(LIB_PATH)
+
+
+def hip_runtimes_loaded():
+    """Paths of the HIP runtime libraries mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
+if len(hip_runtimes_loaded()) > 1:
+    raise ImportError("two HIP runtimes are loaded in this process "
+                      f"({hip_runtimes_loaded()}); load libsattn only through this module")
 
 # names and signatures as declared in include/sattn.h
 _lib.sattn_fwd.restype = ctypes.c_int

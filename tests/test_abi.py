@@ -140,3 +140,17 @@ def test_product_path_has_no_oracle_or_fallback():
             assert "importlib" not in src, name
     src = open(os.path.join(pkg, "sattn.py")).read()
     assert "raise ImportError" in src
+
+
+def test_binding_loads_a_single_hip_runtime():
+    """Importing the binding before torch must not map a second HIP runtime
+    next to torch's own (two runtimes driving one GPU crash the process)."""
+    import subprocess
+    import sys
+    code = ("from causal_attention_forward_amd import sattn\n"
+            "import torch\n"
+            "print(len(sattn.hip_runtimes_loaded()))\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip().splitlines()[-1] == "1"
