@@ -19,28 +19,38 @@
 //  * The K rows feeding S^T are permuted (the `krow` map below) so that the
 //    eight keys a lane holds for each 16-key slice of P^T are consecutive:
 //    the matching V^T operand is then one 16-byte LDS read.
-//  * A workgroup is four wave64s.  Each wave owns 32 query rows of one query
-//    head; the workgroup's waves are GW query heads of one GQA group times
-//    4/GW row blocks, so one K/V tile in LDS feeds 128 query rows.
-//  * Each wave is software-pipelined: while its VALUs turn the scores of tile
-//    j into P, the matrix cores already form the scores of tile j+1, and the
-//    P V products of tile j overlap the row sum.  K and V^T tiles (64 keys)
-//    go through a ring of three LDS buffers (tile j's V^T and tile j+1's K
-//    are read while tile j+2 is written), one barrier per tile; global loads
-//    run one tile ahead of the ring.  LDS rows are padded to 144 bytes so the
-//    16-byte operand reads of 16 lanes hit 64 distinct banks.  K is read
-//    through a buffer descriptor whose range ends at T, so rows past T
-//    arrive as zeros.
-//  * The reference maximum is moved lazily: l and O are rescaled only when
-//    some row's tile maximum exceeds its reference by more than kLazy (base-2
-//    units).  The merge rule holds for any reference, so this changes only
-//    rounding, and P stays below 2^kLazy (far inside binary16).
-//  * Tiles past the causal diagonal are never visited, waves whose rows end
-//    before a tile skip its arithmetic, and only tiles that cross the
-//    diagonal are masked.  Rows past T are computed on zero queries and not
-//    stored, so T need not be a multiple of 64.
-//  * A workgroup takes row tiles b and n-1-b (n row tiles per head), so all
-//    workgroups carry the same causal work and finish together.
+//  * A wave owns 32 query rows of one head.  A workgroup is NW = 8 waves (one
+//    per CU) or, when that would leave CUs idle, NW = 4 (two per CU); its
+//    waves are GW query heads of one GQA group times NW/GW row slots, so each
+//    K/V tile staged in LDS feeds all of them.  Query rows come in 32-row
+//    blocks; a slot takes block n-1-p (heavy) and then block p (light), so
+//    every workgroup carries the same causal work.
+//  * Each wave is software-pipelined: step j forms P V of tile j-1 and S of
+//    tile j+1 on the matrix cores while its VALUs turn S of tile j into P.
+//    The step is laid out by hand (scheduling barriers): each of its 16
+//    matrix products reads its LDS operand four products ahead and is
+//    followed by the exponentials of two scores.  Two register sets of S and
+//    of binary16 P alternate between steps, so no copies carry them.
+//  * K tiles live in a 4-buffer LDS ring (tile t is read at steps t-1 and t),
+//    V^T tiles in a 3-buffer ring (read at step t+1); one barrier per step.
+//    Global loads run two steps ahead of their LDS stores through two
+//    register sets, and every step issues the same loads (tiles past the end
+//    read as zeros through buffer-descriptor range checks), so the waits on
+//    them stay exact.  LDS rows are padded to 144 bytes so the 16-byte
+//    operand reads of 16 lanes hit 64 distinct banks.
+//  * The reference maximum is moved lazily.  P is formed against the current
+//    reference; only when some lane's partial row sum leaves (0, 2^kLazy] is
+//    the reference raised, by the power of two that brings the row's largest
+//    P to at most 1 (exact scaling of P, l and O), or, if a P overflowed
+//    binary32, from the tile's maximum score.  The merge rule holds for any
+//    reference, so this changes only rounding, and P stays at most 2^kLazy.
+//  * Tiles past the causal diagonal are never visited and only a query
+//    block's last tile (the one crossing its diagonal) is masked.  Rows past
+//    T are computed on zero queries and not stored, so T need not be a
+//    multiple of 64.
+//  * Workgroups are dealt to the eight XCDs round-robin; they are renumbered
+//    so that each XCD receives a contiguous run ordered K/V head first,
+//    keeping one K/V head's tiles in one XCD's L2.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -63,19 +73,48 @@ typedef int int4v __attribute__((ext_vector_type(4)));
 
 constexpr int kD = SATTN_HEAD_DIM;  // head width
 constexpr int kBN = 64;             // keys per tile
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kRowHalfs = kD + 8;                // LDS row: 64 values + 16 bytes of padding
 constexpr int kTileHalfs = kBN * kRowHalfs;      // one K or V^T tile in LDS
 constexpr float kLazy = 8.0f;                    // rescale threshold, base-2 units
 constexpr int kBufferWord3 = 0x00020000;         // raw buffer, 32-bit data format
 constexpr int kXcds = 8;                         // accelerator complex dies per MI355X
+constexpr int kCus = 256;                        // compute units per MI355X
 
 __device__ __forceinline__ half8 to_half8(float8v x) { return __builtin_convertvector(x, half8); }
 
 __device__ __forceinline__ float16v mfma(half8 a, half8 b, float16v c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
+
+// Maximum of 32 values as a tree of v_max3 (depth 5 instead of a 16-long
+// dependent chain).
+__device__ __forceinline__ float max32(const float16v& a, const float16v& b) {
+  float t[8], u[4], w[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] = __builtin_fmaxf(__builtin_fmaxf(a[i], a[i + 8]), b[i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) u[i] = __builtin_fmaxf(__builtin_fmaxf(t[i], t[i + 4]), b[8 + i]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) w[i] = __builtin_fmaxf(__builtin_fmaxf(u[i], u[i + 2]), b[12 + i]);
+  return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(w[0], w[1]), b[14]), b[15]);
+}
+
+// Sum of 32 values as a pairwise tree (depth 5).
+__device__ __forceinline__ float sum32(const float16v& a, const float16v& b) {
+  float t[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) t[i] = a[i] + b[i];
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w; ++i) t[i] += t[i + w];
+  return t[0];
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): callers wait
+// for what the barrier publishes themselves, so global loads meant to stay in
+// flight across it are not waited for.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // The value held by the lane whose byte address (lane index * 4) is `addr`.
 __device__ __forceinline__ float xlane(float x, int addr) {
@@ -89,31 +128,36 @@ __device__ __forceinline__ int krow(int m) {
   return 16 * (a >> 1) + 8 * e + 4 * (a & 1) + b;
 }
 
-template <int GW, bool VT_VEC>
-__global__ void __launch_bounds__(kThreads, 2)
+template <int NW, int GW, bool VT_VEC>
+__global__ void __launch_bounds__(64 * NW, 8 / NW)
 sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
                  const half_t* __restrict__ Vt, half_t* __restrict__ O, float* __restrict__ L,
                  float c, int T, int Hq, int Hkv, int G, int nBlocks, int nPairs, int nSlotGroups,
                  int nHeadGroups) {
-  constexpr int RS = kWaves / GW;           // row slots per workgroup
-  constexpr int kBufHalfs = 2 * kTileHalfs;  // one LDS buffer: K tile, then V^T tile
-  __shared__ __attribute__((aligned(16))) half_t smem[2 * kBufHalfs];
+  constexpr int RS = NW / GW;              // row slots per workgroup
+  constexpr int kKRing = 4;                // K tile t is read at steps t-1 and t
+  constexpr int kVRing = 3;                // V^T tile t is read at step t+1
+  constexpr float kSumCap = 256.0f;        // 2^kLazy
+  constexpr int kOutOfRange = 0x7FFFFFF0;  // a buffer offset past every range
+  __shared__ __attribute__((aligned(16))) half_t smem[(kKRing + kVRing) * kTileHalfs];
+  half_t* const kring = smem;
+  half_t* const vring = smem + kKRing * kTileHalfs;
+  constexpr int kTileBytes = kTileHalfs * 2;
+  // LDS operand of ring buffer `buf` at byte offset `off` from the lane's base.
+  // The buffer offset goes through readfirstlane so that it stays one scalar
+  // per step instead of a per-lane induction variable per read.
+  auto lds8 = [&](const half_t* ring, int buf, int laneByte, int off) -> half8 {
+    const int b = __builtin_amdgcn_readfirstlane(buf * kTileBytes);
+    return *reinterpret_cast<const half8*>(reinterpret_cast<const char*>(ring) + laneByte + b +
+                                           off);
+  };
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int n = lane & 31;  // accumulator column (query) / operand row
-  const int g = lane >> 5;  // operand k-half / accumulator row octet
+  const int n = lane & 31;
+  const int g = lane >> 5;
 
-  // Query rows come in 32-row blocks; block b is paired with block
-  // nBlocks-1-b, so the two together always need about nBlocks/2 + 1 key
-  // tiles.  A wave owns one pair (its query tiles 0 and 1) of one head; the
-  // workgroup's waves are GW heads of one GQA group times RS pairs.
-  //
-  // Workgroups are dealt to the eight XCDs round-robin (workgroup b runs on
-  // XCD b % 8); renumbering them so that each XCD receives a contiguous run
-  // of logical ids, ordered K/V head first, keeps one K/V head's tiles in
-  // one XCD's L2.
   const int nWg = gridDim.x;
   const int xcd = blockIdx.x % kXcds, idx = blockIdx.x / kXcds;
   const int lid = xcd * (nWg / kXcds) + min(xcd, nWg % kXcds) + idx;
@@ -122,237 +166,346 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
   const int hg = (lid - kv * perKv) / nSlotGroups;
   const int sg = lid - kv * perKv - hg * nSlotGroups;
   const int h = kv * G + hg * GW + (wave % GW);
-  const int pair = sg * RS + wave / GW;
-  const bool hasPair = pair < nPairs;
-  const int blk0 = pair;                     // light block
-  const int blk1 = nBlocks - 1 - pair;       // heavy block (== blk0 for an odd middle)
-  const int rq[2] = {32 * blk0, 32 * blk1};  // first row of query tiles 0 and 1
-  // key tiles each query tile needs (0 when the tile does not exist)
-  const int need0 = hasPair ? min(T - 1, rq[0] + 31) / kBN + 1 : 0;
-  const int need1 = (hasPair && blk1 > blk0) ? min(T - 1, rq[1] + 31) / kBN + 1 : 0;
-  // key tiles the workgroup walks: the need of its first slot's heavy block,
-  // the largest of its waves
-  const int nkt = min(T - 1, 32 * (nBlocks - 1 - sg * RS) + 31) / kBN + 1;
+  const int slot = wave / GW;
 
-  // Global -> register staging of one tile: 512 K chunks and 512 V^T chunks
-  // of 16 bytes; thread t owns chunks t and t + 256 of each (rows cr, cr + 32,
-  // column chunk cc).  Both planes are read through buffer descriptors: K's
-  // range ends at row T, so rows past T arrive as zeros; V^T tiles wholly
-  // inside T take their key offset as a scalar, and the one partial tile is
-  // read with per-element guards.
+  auto block_of = [&](int task, int s) -> int {
+    const int p = sg * RS + s;
+    if (p >= nPairs) return -1;
+    const int hi = nBlocks - 1 - p;
+    return task == 0 ? hi : (p < hi ? p : -1);
+  };
+  auto need_of = [&](int blk) -> int { return blk < 0 ? 0 : min(T - 1, 32 * blk + 31) / kBN + 1; };
+
+  // Global -> register staging: thread t owns 16-byte chunk t of a K tile and
+  // of a V^T tile (row cr, column chunk cc).  Two register sets, by stage
+  // parity, keep loads two steps ahead of their LDS stores.
+  constexpr int kCpt = 8 / NW;          // 16-byte chunks per thread per tile
+  constexpr int kRowsPerPass = 8 * NW;  // tile rows one pass of the workgroup covers
   const int cr = tid >> 3, cc = tid & 7;
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<half_t*>(K + (size_t)kv * T * kD), 0, T * kD * 2, kBufferWord3);
   const half_t* Vh = Vt + (size_t)kv * kD * T;
   const __amdgpu_buffer_rsrc_t vrsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(Vh), 0, kD * T * 2, kBufferWord3);
-  const int kByte = (cr * kD + cc * 8) * 2;   // + 32*128 for the second chunk, + key0*128
-  const int vByte = (cr * T + cc * 8) * 2;    // + 32*T*2 for the second chunk, + key0*2
-  int4v stK[2], stV[2];
-  auto load_tile = [&](int kt) {
+  const int kByte = (cr * kD + cc * 8) * 2;
+  const int vByte = (cr * T + cc * 8) * 2;
+  typedef int4v Stage[kCpt];
+  auto load_k = [&](int kt, Stage& dst) {
+#pragma unroll
+    for (int p = 0; p < kCpt; ++p)
+      dst[p] = __builtin_amdgcn_raw_buffer_load_b128(
+          krsrc, kByte + p * kRowsPerPass * kD * 2,
+          __builtin_amdgcn_readfirstlane(kt * kBN * kD * 2), 0);
+  };
+  // V^T chunks at or past T (T % 8 == 0: a chunk is wholly inside or
+  // outside) take an offset past the buffer's range and read as zeros, so
+  // every stage issues the same loads and the waits stay exact.
+  auto load_v = [&](int kt, Stage& dst) {
     const int key0 = kt * kBN;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      stK[p] = __builtin_amdgcn_raw_buffer_load_b128(krsrc, kByte + (key0 + 32 * p) * kD * 2, 0, 0);
-      if (key0 + kBN <= T) {  // whole tile inside T (uniform)
-        stV[p] = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, vByte + 32 * p * T * 2, key0 * 2, 0);
+    for (int p = 0; p < kCpt; ++p) {
+      const int rb = vByte + p * kRowsPerPass * T * 2;
+      if (VT_VEC) {
+        const int off = key0 + cc * 8 < T ? rb : kOutOfRange;
+        dst[p] = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off,
+                                                       __builtin_amdgcn_readfirstlane(key0 * 2), 0);
+      } else if (key0 + kBN <= T) {
+        dst[p] = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, rb, key0 * 2, 0);
       } else {
-        const half_t* vsrc = Vh + (size_t)(cr + 32 * p) * T + key0 + cc * 8;  // V^T row d
-        if (VT_VEC) {  // T % 8 == 0: a chunk is wholly inside or outside
-          stV[p] = key0 + cc * 8 < T ? *reinterpret_cast<const int4v*>(vsrc) : int4v{};
-        } else {
-          half8 v;
+        const half_t* vsrc = Vh + (size_t)(cr + p * kRowsPerPass) * T + key0 + cc * 8;
+        half8 v;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (key0 + cc * 8 + e < T) ? vsrc[e] : (half_t)0;
-          stV[p] = __builtin_bit_cast(int4v, v);
-        }
+        for (int e = 0; e < 8; ++e) v[e] = (key0 + cc * 8 + e < T) ? vsrc[e] : (half_t)0;
+        dst[p] = __builtin_bit_cast(int4v, v);
       }
     }
   };
-  const int stOff = cr * kRowHalfs + cc * 8;  // + 32 rows for the second chunk
-  auto store_tile = [&](int buf) {
-    half_t* ks = smem + buf * kBufHalfs;
+  const int stOff = cr * kRowHalfs + cc * 8;
+  auto store_k = [&](int buf, const Stage& src) {
+    const int b = __builtin_amdgcn_readfirstlane(buf * kTileBytes);
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      *reinterpret_cast<int4v*>(ks + stOff + 32 * p * kRowHalfs) = stK[p];
-      *reinterpret_cast<int4v*>(ks + kTileHalfs + stOff + 32 * p * kRowHalfs) = stV[p];
-    }
+    for (int p = 0; p < kCpt; ++p)
+      *reinterpret_cast<int4v*>(reinterpret_cast<char*>(kring) + b +
+                                (stOff + p * kRowsPerPass * kRowHalfs) * 2) = src[p];
+  };
+  auto store_v = [&](int buf, const Stage& src) {
+    const int b = __builtin_amdgcn_readfirstlane(buf * kTileBytes);
+#pragma unroll
+    for (int p = 0; p < kCpt; ++p)
+      *reinterpret_cast<int4v*>(reinterpret_cast<char*>(vring) + b +
+                                (stOff + p * kRowsPerPass * kRowHalfs) * 2) = src[p];
   };
 
-  const int swapAddr = (lane ^ 32) << 2;  // byte address of the lane 32 away
+  const int swapAddr = (lane ^ 32) << 2;
+  const int kOff = krow(n) * kRowHalfs + 8 * g;
+  const int vOff = n * kRowHalfs + 8 * g;
 
-  // Per-lane LDS operand offsets (halfs) within a tile.
-  const int kOff = krow(n) * kRowHalfs + 8 * g;  // + 32s rows, + 16kk columns
-  const int vOff = n * kRowHalfs + 8 * g;        // + 32dt rows, + 16ks columns
+#pragma nounroll
+  for (int task = 0; task < 2; ++task) {
+    int nkt = 0;
+#pragma unroll
+    for (int s = 0; s < RS; ++s) nkt = max(nkt, need_of(block_of(task, s)));
+    if (nkt == 0) break;
+    const int blk = block_of(task, slot);
+    const int need = need_of(blk);
+    const int row = 32 * max(blk, 0) + n;
 
-  // Q^T as the B operand of S^T = K Q^T: lane (n, g) of query tile qt holds
-  // Q[rq[qt] + n][16kk + 8g .. +8].
-  half8 qf[2][4];
+    half8 qf[4];
+    {
+      const half_t* qrow = Q + ((size_t)h * T + row) * kD + 8 * g;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int row = rq[qt] + n;
-    const bool live = qt == 0 ? need0 > 0 : need1 > 0;
-    const half_t* qrow = Q + ((size_t)h * T + row) * kD + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      qf[qt][kk] = (live && row < T) ? *reinterpret_cast<const half8*>(qrow + 16 * kk) : half8{};
-  }
-
-  float m[2], l[2];     // reference maximum of t (base 2) and this lane's partial row sum
-  float16v o[2][2];     // O^T per query tile: d rows 0..31 and 32..63 of this lane's query
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    m[qt] = -INFINITY;
-    l[qt] = 0.0f;
-    o[qt][0] = float16v{};
-    o[qt][1] = float16v{};
-  }
-
-  // Key tile j (in LDS buffer `buf`) folded into the live query tiles
-  // A0, A1: every K and V^T operand read from LDS feeds each live tile.
-  auto tile_body = [&](auto A0, auto A1, int j, int buf) {
-    constexpr bool a0 = decltype(A0)::value, a1 = decltype(A1)::value;
-    const bool act[2] = {a0, a1};
-    const int key0 = j * kBN;
-    const half_t* ks = smem + buf * kBufHalfs;
-    const half_t* vs = ks + kTileHalfs;
-
-    // S^T (keys x queries): element i of S[qt][sb] is key key0 + 32sb + 16*(i/8) + 8g + i%8.
-    float16v S[2][2];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const half8 a = *reinterpret_cast<const half8*>(ks + kOff + 32 * sb * kRowHalfs + 16 * kk);
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-          if (act[qt]) S[qt][sb] = mfma(a, qf[qt][kk], kk == 0 ? float16v{} : S[qt][sb]);
-      }
+      for (int kk = 0; kk < 4; ++kk)
+        qf[kk] = (need > 0 && row < T) ? *reinterpret_cast<const half8*>(qrow + 16 * kk) : half8{};
     }
+    float m = -INFINITY, l = 0.0f;
+    float16v o0 = {}, o1 = {};
+    float16v sa0, sa1, sb0, sb1;
+    half8 pa[4], pb[4];
 
-    float mx[2];
-    bool grow = false;
+    auto scores = [&](int buf, float16v& r0, float16v& r1) {
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      if (!act[qt]) continue;
-      float16v& s0 = S[qt][0];
-      float16v& s1 = S[qt][1];
-      // Causal mask on tiles that reach past the query tile's first row.
-      if (key0 + kBN - 1 > rq[qt]) {
-        const int lim = rq[qt] + n - key0 - 8 * g;  // element i masked when 16*(i/8) + i%8 (+32) > lim
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int k = 16 * (i >> 3) + (i & 7);
-          if (k > lim) s0[i] = -INFINITY;
-          if (k + 32 > lim) s1[i] = -INFINITY;
-        }
+      for (int kk = 0; kk < 4; ++kk) {
+        const half8 a0 = lds8(kring, buf, kOff * 2, 32 * kk);
+        const half8 a1 = lds8(kring, buf, kOff * 2, (32 * kRowHalfs + 16 * kk) * 2);
+        r0 = mfma(a0, qf[kk], kk == 0 ? float16v{} : r0);
+        r1 = mfma(a1, qf[kk], kk == 0 ? float16v{} : r1);
       }
-      // The tile's row maximum (raw scores; c > 0 keeps the order), both lane halves.
-      float x = __builtin_fmaxf(s0[0], s1[0]);
+    };
+    auto pv = [&](int buf, const half8 (&p)[4]) {
 #pragma unroll
-      for (int i = 1; i < 16; ++i) x = __builtin_fmaxf(x, __builtin_fmaxf(s0[i], s1[i]));
-      mx[qt] = __builtin_fmaxf(x, xlane(x, swapAddr)) * c;
-      grow |= mx[qt] > m[qt] + kLazy;
-    }
-
-    // Move the reference only when some row of the wave outgrew it by kLazy.
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        if (!act[qt]) continue;
-        const float m_new = __builtin_fmaxf(m[qt], mx[qt]);
-        const float alpha = __builtin_amdgcn_exp2f(m[qt] - m_new);  // 0 on a row's first tile
-        m[qt] = m_new;
-        l[qt] *= alpha;
-        o[qt][0] *= alpha;
-        o[qt][1] *= alpha;
+      for (int ks4 = 0; ks4 < 4; ++ks4) {
+        const half8 v0 = lds8(vring, buf, vOff * 2, 32 * ks4);
+        const half8 v1 = lds8(vring, buf, vOff * 2, (32 * kRowHalfs + 16 * ks4) * 2);
+        o0 = mfma(v0, p[ks4], o0);
+        o1 = mfma(v1, p[ks4], o1);
       }
-    }
-
-    // P = 2^(S c - m), rounded to binary16 for the product with V: slice ks
-    // of query tile qt holds keys 16ks + 8g .. +7.
-    half8 pb[2][4];
+    };
+    auto mask = [&](int j, float16v& s0, float16v& s1) {
+      const int lim = row - j * kBN - 8 * g;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      if (!act[qt]) continue;
-      float16v& s0 = S[qt][0];
-      float16v& s1 = S[qt][1];
-      const float neg_m = -m[qt];
+      for (int i = 0; i < 16; ++i) {
+        const int k = 16 * (i >> 3) + (i & 7);
+        if (k > lim) s0[i] = -INFINITY;
+        if (k + 32 > lim) s1[i] = -INFINITY;
+      }
+    };
+    auto exp_tile = [&](float16v& s0, float16v& s1) -> float {
+      const float neg_m = -m;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c, neg_m));
         s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, neg_m));
       }
-      pb[qt][0] = to_half8(__builtin_shufflevector(s0, s0, 0, 1, 2, 3, 4, 5, 6, 7));
-      pb[qt][1] = to_half8(__builtin_shufflevector(s0, s0, 8, 9, 10, 11, 12, 13, 14, 15));
-      pb[qt][2] = to_half8(__builtin_shufflevector(s1, s1, 0, 1, 2, 3, 4, 5, 6, 7));
-      pb[qt][3] = to_half8(__builtin_shufflevector(s1, s1, 8, 9, 10, 11, 12, 13, 14, 15));
-    }
+      return sum32(s0, s1);
+    };
+    auto round_p = [&](const float16v& s0, const float16v& s1, half8 (&p)[4]) {
+      p[0] = to_half8(__builtin_shufflevector(s0, s0, 0, 1, 2, 3, 4, 5, 6, 7));
+      p[1] = to_half8(__builtin_shufflevector(s0, s0, 8, 9, 10, 11, 12, 13, 14, 15));
+      p[2] = to_half8(__builtin_shufflevector(s1, s1, 0, 1, 2, 3, 4, 5, 6, 7));
+      p[3] = to_half8(__builtin_shufflevector(s1, s1, 8, 9, 10, 11, 12, 13, 14, 15));
+    };
+    auto exact_reference = [&](const float16v& s0, const float16v& s1) {
+      const float x = max32(s0, s1);
+      const float mx = __builtin_fmaxf(x, xlane(x, swapAddr)) * c;
+      const float m_new = __builtin_fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 when m = -inf
+      m = m_new;
+      l *= alpha;
+      o0 *= alpha;
+      o1 *= alpha;
+    };
 
-    // O^T += V^T P^T over four 16-key slices, overlapping the row sums of P.
+    // Step j >= 1: P V of tile j-1 (pin), S of tile j+1 into x (SN), P of
+    // tile j from its scores in s into pout (masked on the query block's
+    // last tile).  The fast path is laid out by hand: the LDS operand of
+    // each matrix product is read four products ahead, and every product is
+    // followed by the softmax of two score elements; scheduling barriers
+    // keep that order.
+    auto step = [&](auto SNF, auto MASKF, int j, float16v& s0, float16v& s1, float16v& x0,
+                    float16v& x1, const half8 (&pin)[4], half8 (&pout)[4]) {
+      constexpr bool kSn = decltype(SNF)::value, kMask = decltype(MASKF)::value;
+      constexpr int kM = kSn ? 16 : 8;  // matrix products this step
+      const int vbuf = (j + kVRing - 1) % kVRing, kbuf = (j + 1) % kKRing;
+      auto rd = [&](int i) -> half8 {
+        if (i < 8)  // V^T operand of P V: slice ks4 = i/2, d rows 32*(i%2)
+          return lds8(vring, vbuf, vOff * 2, (32 * (i & 1) * kRowHalfs + 16 * (i >> 1)) * 2);
+        const int kk = (i - 8) >> 1, sb = i & 1;  // K operand of S: k-step kk, key rows 32*sb
+        return lds8(kring, kbuf, kOff * 2, (32 * sb * kRowHalfs + 16 * kk) * 2);
+      };
+      if constexpr (kMask) mask(j, s0, s1);
+      const float neg_m = -m;
+      half8 r[4];
 #pragma unroll
-    for (int ks4 = 0; ks4 < 4; ++ks4) {
+      for (int i = 0; i < 4; ++i) r[i] = rd(i);
+      float acc[4];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const half8 v = *reinterpret_cast<const half8*>(vs + vOff + 32 * dt * kRowHalfs + 16 * ks4);
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-          if (act[qt]) o[qt][dt] = mfma(v, pb[qt][ks4], o[qt][dt]);
+      for (int i = 0; i < 16; ++i) {
+        if (i < kM) {
+          const half8 a = r[i & 3];
+          if (i < 8) {
+            if (i & 1) o1 = mfma(a, pin[i >> 1], o1);
+            else o0 = mfma(a, pin[i >> 1], o0);
+          } else {
+            const int kk = (i - 8) >> 1;
+            if (i & 1) x1 = mfma(a, qf[kk], kk == 0 ? float16v{} : x1);
+            else x0 = mfma(a, qf[kk], kk == 0 ? float16v{} : x0);
+          }
+          if (i + 4 < kM) r[i & 3] = rd(i + 4);
+        }
+        // softmax of elements 2i, 2i+1 (s0 for i < 8, s1 after)
+        float t;
+        if (i < 8) {
+          s0[2 * i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[2 * i], c, neg_m));
+          s0[2 * i + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[2 * i + 1], c, neg_m));
+          t = s0[2 * i] + s0[2 * i + 1];
+        } else {
+          s1[2 * i - 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[2 * i - 16], c, neg_m));
+          s1[2 * i - 15] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[2 * i - 15], c, neg_m));
+          t = s1[2 * i - 16] + s1[2 * i - 15];
+        }
+        acc[i & 3] = i < 4 ? t : acc[i & 3] + t;
+        if ((i & 3) == 3) {
+          const float16v& sv = i < 8 ? s0 : s1;  // binary16 P of keys 8(i/4 % 2) + 0..7
+          const float8v v8 = (i & 4) ? __builtin_shufflevector(sv, sv, 8, 9, 10, 11, 12, 13, 14, 15)
+                                     : __builtin_shufflevector(sv, sv, 0, 1, 2, 3, 4, 5, 6, 7);
+          pout[i >> 2] = to_half8(v8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      if (!act[qt]) continue;
-      float ls0 = S[qt][0][0], ls1 = S[qt][1][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) {
-        ls0 += S[qt][0][i];
-        ls1 += S[qt][1][i];
+      float lsum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      const bool over = __builtin_amdgcn_ballot_w64(!(lsum <= kSumCap)) != 0;
+      // Pins the binary16 P in this block: the fp32 P dies here on the fast
+      // path, and only pout merges with the slow path.
+      asm volatile("" ::"v"(pout[0]), "v"(pout[1]), "v"(pout[2]), "v"(pout[3]));
+      if (over) {
+        asm volatile("");  // keeps the slow path a branch, never speculated
+        // Some row's partial sum left (0, 2^kLazy].  Move each row's
+        // reference up by the power of two that brings its largest P to at
+        // most 1; exact scaling of P, l and O.  If a P overflowed binary32,
+        // S is formed again from K (still in the ring) and the reference is
+        // taken from the tile maximum.
+        const float x = max32(s0, s1);
+        const float pmax = __builtin_fmaxf(x, xlane(x, swapAddr));
+        if (__builtin_amdgcn_ballot_w64(!(pmax < INFINITY)) == 0) {
+          const int e = pmax > 1.0f ? __builtin_amdgcn_frexp_expf(pmax) : 0;
+          const float alpha = __builtin_ldexpf(1.0f, -e);
+          m += (float)e;
+          l *= alpha;
+          o0 *= alpha;
+          o1 *= alpha;
+          s0 *= alpha;
+          s1 *= alpha;
+          lsum = sum32(s0, s1);
+        } else {
+          scores(j % kKRing, s0, s1);
+          if constexpr (kMask) mask(j, s0, s1);
+          exact_reference(s0, s1);
+          lsum = exp_tile(s0, s1);
+        }
+        round_p(s0, s1, pout);
       }
-      l[qt] += ls0 + ls1;
-    }
-  };
+      l += lsum;
+    };
 
-  using T1 = std::integral_constant<bool, true>;
-  using F0 = std::integral_constant<bool, false>;
-  load_tile(0);
-  store_tile(0);
-  for (int j = 0; j < nkt; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nkt) load_tile(j + 1);
-    __syncthreads();
-    const bool a0 = j < need0, a1 = j < need1;
-    if (a0 && a1)
-      tile_body(T1{}, T1{}, j, buf);
-    else if (a1)
-      tile_body(F0{}, T1{}, j, buf);
-    else if (a0)
-      tile_body(T1{}, F0{}, j, buf);
-    if (j + 1 < nkt) store_tile(buf ^ 1);
-  }
-
-  // Epilogue: the row sum over both lane halves, O / l, and m + log2 l.
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    if ((qt == 0 ? need0 : need1) == 0) continue;
-    const int row = rq[qt] + n;
-    const float lt = l[qt] + xlane(l[qt], swapAddr);
-    const float inv = __builtin_amdgcn_rcpf(lt);
-    const float lse = m[qt] + __builtin_amdgcn_logf(lt);
-    if (row < T) {
-      half_t* orow = O + (size_t)row * Hq * kD + (size_t)h * kD + 4 * g;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        // accumulator elements 4q4 .. 4q4+3 are d = 8q4 + 4g + 0..3 (+32 in o[qt][1])
-        const float16v& a = o[qt][0];
-        const float16v& b = o[qt][1];
-        const float4v va = {a[4 * q4], a[4 * q4 + 1], a[4 * q4 + 2], a[4 * q4 + 3]};
-        const float4v vb = {b[4 * q4], b[4 * q4 + 1], b[4 * q4 + 2], b[4 * q4 + 3]};
-        *reinterpret_cast<half4*>(orow + 8 * q4) = __builtin_convertvector(va * inv, half4);
-        *reinterpret_cast<half4*>(orow + 32 + 8 * q4) = __builtin_convertvector(vb * inv, half4);
-      }
-      if (g == 0) L[(size_t)h * T + row] = lse;
+    // Ring schedule: K tile t is read at steps t-1 (S of t) and t (overflow
+    // fallback), V^T tile t at step t+1 (P V of t).  Stage j writes K of tile
+    // j+2 and V^T of tile j (loaded at stage j-2 into register set j % 2) into
+    // buffers last read at step j-2, then loads K of tile j+4 and V^T of tile
+    // j+2 into the same set; one barrier per step.
+    Stage setK[2], setV[2];
+    load_k(0, setK[0]);
+    store_k(0, setK[0]);
+    load_k(1, setK[1]);
+    store_k(1, setK[1]);
+    load_k(2, setK[0]);
+    load_v(0, setV[0]);
+    load_k(3, setK[1]);
+    load_v(1, setV[1]);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    barrier();
+    // Loads past the last tile read zeros and stores of them land in ring
+    // buffers that are free by the same argument as real tiles, so a stage
+    // has no branches.
+    auto stage = [&](auto PARF, int j) {
+      constexpr int P = decltype(PARF)::value;
+      store_k((j + 2) % kKRing, setK[P]);
+      store_v(j % kVRing, setV[P]);
+      load_k(j + 4, setK[P]);
+      load_v(j + 2, setV[P]);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      barrier();
+    };
+    using T1 = std::integral_constant<bool, true>;
+    using F0 = std::integral_constant<bool, false>;
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    auto stage_any = [&](int j) {
+      if (j & 1) stage(P1{}, j);
+      else stage(P0{}, j);
+    };
+    // step 0: S of tiles 0 and 1, P of tile 0 from its exact maximum
+    if (need > 0) scores(0, sa0, sa1);
+    stage(P0{}, 0);
+    if (need > 1) {
+      scores(1, sb0, sb1);
+      exact_reference(sa0, sa1);
+      l += exp_tile(sa0, sa1);
+      round_p(sa0, sa1, pa);
+    } else if (need == 1) {
+      mask(0, sa0, sa1);
+      exact_reference(sa0, sa1);
+      l += exp_tile(sa0, sa1);
+      round_p(sa0, sa1, pa);
     }
+    // Every wave runs stage(j) for j = 1 .. nkt in order (the workgroup's
+    // barriers); its own steps end at its own last tile: steady steps
+    // 1 .. need-2 (two per trip, S and P sets alternating), the masked step
+    // need-1, then P V of tile need-1 and the epilogue at step need.
+    int j = 1;
+    for (; j + 2 < need; j += 2) {
+      stage(P1{}, j);
+      step(T1{}, F0{}, j, sb0, sb1, sa0, sa1, pa, pb);
+      stage(P0{}, j + 1);
+      step(T1{}, F0{}, j + 1, sa0, sa1, sb0, sb1, pb, pa);
+    }
+    if (j + 1 < need) {
+      stage(P1{}, j);
+      step(T1{}, F0{}, j, sb0, sb1, sa0, sa1, pa, pb);
+      ++j;
+      sb0 = sa0;
+      sb1 = sa1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pa[i] = pb[i];
+    }
+    if (j + 1 == need) {
+      stage_any(j);
+      step(F0{}, T1{}, j, sb0, sb1, sa0, sa1, pa, pb);
+      ++j;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pa[i] = pb[i];
+    }
+    if (need > 0) {
+      stage_any(j);
+      pv((j + kVRing - 1) % kVRing, pa);
+      const float lt = l + xlane(l, swapAddr);
+      const float inv = __builtin_amdgcn_rcpf(lt);
+      const float lse = m + __builtin_amdgcn_logf(lt);
+      if (row < T) {
+        half_t* orow = O + (size_t)row * Hq * kD + (size_t)h * kD + 4 * g;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4v va = {o0[4 * q4], o0[4 * q4 + 1], o0[4 * q4 + 2], o0[4 * q4 + 3]};
+          const float4v vb = {o1[4 * q4], o1[4 * q4 + 1], o1[4 * q4 + 2], o1[4 * q4 + 3]};
+          *reinterpret_cast<half4*>(orow + 8 * q4) = __builtin_convertvector(va * inv, half4);
+          *reinterpret_cast<half4*>(orow + 32 + 8 * q4) = __builtin_convertvector(vb * inv, half4);
+        }
+        if (g == 0) L[(size_t)h * T + row] = lse;
+      }
+      ++j;
+    }
+    for (; j <= nkt; ++j) stage_any(j);
+    barrier();
   }
 }
 
@@ -374,27 +527,42 @@ int check_device() {
   return ok ? SATTN_OK : SATTN_ERR_DEVICE;
 }
 
-template <int GW, bool VT_VEC>
+template <int NW, int GW, bool VT_VEC>
 void launch(const half_t* Q, const half_t* K, const half_t* Vt, half_t* O, float* L, float c,
             int T, int Hq, int Hkv, hipStream_t stream) {
-  constexpr int RS = kWaves / GW;
+  constexpr int RS = NW / GW;
   const int G = Hq / Hkv;
   const int nBlocks = (T + 31) / 32;
   const int nPairs = (nBlocks + 1) / 2;
   const int nSlotGroups = (nPairs + RS - 1) / RS;
   const int nHeadGroups = G / GW;
   const unsigned grid = (unsigned)nSlotGroups * (unsigned)Hkv * (unsigned)nHeadGroups;
-  hipLaunchKernelGGL((sattn_fwd_kernel<GW, VT_VEC>), dim3(grid), dim3(kThreads), 0, stream, Q, K,
-                     Vt, O, L, c, T, Hq, Hkv, G, nBlocks, nPairs, nSlotGroups, nHeadGroups);
+  hipLaunchKernelGGL((sattn_fwd_kernel<NW, GW, VT_VEC>), dim3(grid), dim3(64 * NW), 0, stream, Q,
+                     K, Vt, O, L, c, T, Hq, Hkv, G, nBlocks, nPairs, nSlotGroups, nHeadGroups);
+}
+
+// Eight-wave workgroups (one per CU) feed each K/V tile to twice the query
+// rows; when they would leave CUs idle, four-wave workgroups (two per CU)
+// double the number of workgroups.
+template <int GW, bool VT_VEC>
+void launch_nw(const half_t* Q, const half_t* K, const half_t* Vt, half_t* O, float* L, float c,
+               int T, int Hq, int Hkv, hipStream_t stream) {
+  const int nPairs = ((T + 31) / 32 + 1) / 2;
+  const long long grid8 =
+      (long long)((nPairs + 8 / GW - 1) / (8 / GW)) * Hkv * ((Hq / Hkv) / GW);
+  if (grid8 >= kCus)
+    launch<8, GW, VT_VEC>(Q, K, Vt, O, L, c, T, Hq, Hkv, stream);
+  else
+    launch<4, GW, VT_VEC>(Q, K, Vt, O, L, c, T, Hq, Hkv, stream);
 }
 
 template <int GW>
 void launch_gw(const half_t* Q, const half_t* K, const half_t* Vt, half_t* O, float* L, float c,
                int T, int Hq, int Hkv, hipStream_t stream) {
   if (T % 8 == 0)
-    launch<GW, true>(Q, K, Vt, O, L, c, T, Hq, Hkv, stream);
+    launch_nw<GW, true>(Q, K, Vt, O, L, c, T, Hq, Hkv, stream);
   else
-    launch<GW, false>(Q, K, Vt, O, L, c, T, Hq, Hkv, stream);
+    launch_nw<GW, false>(Q, K, Vt, O, L, c, T, Hq, Hkv, stream);
 }
 
 }  // namespace
