@@ -7,56 +7,15 @@ sampled rows of every head (the oracle computes those one by one), plus
 properties that hold at any size.
 """
 import math
-import sys
 
 import numpy as np
 import pytest
 
 from causal_attention_forward_amd.inputs import WORKLOADS, make_inputs, make_workload
 from oracle import attention_ref, attention_rows_ref
+from parity_util import TOL_L, TOL_O, assert_close, note, run, sample_rows
 
 pytestmark = pytest.mark.gpu
-
-TOL_O = 4e-3
-TOL_L = 2e-4
-
-
-@pytest.fixture(scope="module")
-def dev():
-    import torch
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
-    return torch.device("cuda:0")
-
-
-@pytest.fixture(scope="module")
-def sattn():
-    from causal_attention_forward_amd import sattn as mod
-    return mod
-
-
-def note(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
-
-
-def run(sattn, dev, x):
-    import torch
-    q = torch.from_numpy(x.Q).to(dev)
-    k = torch.from_numpy(x.K).to(dev)
-    vt = torch.from_numpy(x.Vt).to(dev)
-    O, L = sattn.fwd(q, k, vt, x.c)
-    torch.cuda.synchronize()
-    return O.cpu().numpy().astype(np.float64), L.cpu().numpy().astype(np.float64)
-
-
-def assert_close(O, L, Or, Lr, what):
-    assert np.isfinite(O).all() and np.isfinite(L).all(), what
-    eo = float(np.abs(O - Or).max())
-    el = float(np.abs(L - Lr).max())
-    note(f"  {what}: max|dO|={eo:.3e} max|dL|={el:.3e}")
-    assert eo <= TOL_O, f"{what}: max|dO| = {eo}"
-    assert el <= TOL_L, f"{what}: max|dL| = {el}"
 
 
 @pytest.mark.parametrize("idx", [0, 1, 2])
@@ -67,12 +26,6 @@ def test_workload_full(sattn, dev, idx):
     O, L = run(sattn, dev, x)
     Or, Lr = attention_ref(x.Q, x.K, x.Vt, x.c)
     assert_close(O, L, Or, Lr, w.name)
-
-
-def sample_rows(T, rng, extra=24):
-    fixed = {0, 1, 2, 31, 32, 63, 64, 65, 127, 128, T // 2, T - 65, T - 64, T - 33, T - 2, T - 1}
-    rows = sorted(r for r in fixed | set(rng.integers(0, T, extra).tolist()) if 0 <= r < T)
-    return rows
 
 
 @pytest.mark.parametrize("idx", [3, 4])

@@ -1,0 +1,96 @@
+"""Parity on inputs built to drive the kernel's less common paths, on both
+workgroup shapes (eight waves when the grid fills every CU, four otherwise).
+
+* Rising scores: keys carry a ramp along the sequence, so a row's running
+  maximum grows by several base-2 units per 64-key tile and the reference
+  must be raised again and again (the exact power-of-two rescale).
+* Score spikes: two keys whose scores exceed everything before them by far
+  more than 128 base-2 units, so 2^(t - m) overflows binary32 and the tile's
+  scores are formed again and the reference taken from their maximum; the
+  second spike falls inside the diagonal (masked) tile of some rows.
+* Shapes whose grid selects the eight-wave workgroup with T % 8 != 0, and
+  with two or one query heads per K/V head.
+Full oracle comparison where it runs in seconds, sampled rows otherwise.
+"""
+import numpy as np
+import pytest
+
+from causal_attention_forward_amd.inputs import make_inputs
+from oracle import attention_ref, attention_rows_ref
+from parity_util import TOL_L, TOL_O, assert_close, note, run, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+# (T, Hq, Hkv): the first is a four-wave grid, the second an eight-wave one
+PATH_SHAPES = [(1000, 8, 2), (4096, 32, 8)]
+
+
+def rising(T, Hq, Hkv, seed):
+    """Positive queries and a ramp of 6 * k / T on every element of key k."""
+    x = make_inputs(T, Hq, Hkv, seed=seed)
+    x.Q[:] = (np.abs(x.Q.astype(np.float32)) + 0.25).astype(np.float16)
+    ramp = (6.0 * np.arange(T, dtype=np.float32) / T)[None, :, None]
+    x.K[:] = (x.K.astype(np.float32) + ramp).astype(np.float16)
+    return x
+
+
+def spiked(T, Hq, Hkv, seed):
+    """Positive queries; key T/3 + 5 set to 24 and key 2T/3 + 40 to 40 on
+    every element (scores of about 2000 and 3300, i.e. jumps of hundreds of
+    base-2 units over the running maximum)."""
+    x = make_inputs(T, Hq, Hkv, seed=seed)
+    x.Q[:] = (np.abs(x.Q.astype(np.float32)) + 0.5).astype(np.float16)
+    k1, k2 = T // 3 + 5, 2 * T // 3 + 40
+    x.K[:, k1, :] = np.float16(24.0)
+    x.K[:, k2, :] = np.float16(40.0)
+    return x, (k1, k2)
+
+
+def compare(sattn, dev, x, what, extra_rows=()):
+    O, L = run(sattn, dev, x)
+    if x.T * x.Hq <= 1000 * 8:
+        Or, Lr = attention_ref(x.Q, x.K, x.Vt, x.c)
+        assert_close(O, L, Or, Lr, what)
+        return O, L
+    rng = np.random.default_rng(x.T + x.Hq)
+    worst_o = worst_l = 0.0
+    for h in range(x.Hq):
+        rows = sorted(set(sample_rows(x.T, rng, extra=8)) | {r for r in extra_rows if 0 <= r < x.T})
+        Or, Lr = attention_rows_ref(x.Q, x.K, x.Vt, x.c, h, rows)
+        assert np.isfinite(O[rows]).all() and np.isfinite(L[h, rows]).all()
+        worst_o = max(worst_o, float(np.abs(O[rows, h * 64:(h + 1) * 64] - Or).max()))
+        worst_l = max(worst_l, float(np.abs(L[h, rows] - Lr).max()))
+    note(f"  {what} (sampled rows): max|dO|={worst_o:.3e} max|dL|={worst_l:.3e}")
+    assert worst_o <= TOL_O and worst_l <= TOL_L
+    return O, L
+
+
+@pytest.mark.parametrize("shape", PATH_SHAPES)
+def test_rising_scores(sattn, dev, shape):
+    T, hq, hkv = shape
+    note(f"rising scores T={T} Hq={hq} Hkv={hkv}")
+    x = rising(T, hq, hkv, seed=21)
+    compare(sattn, dev, x, f"rising T={T}")
+
+
+@pytest.mark.parametrize("shape", PATH_SHAPES)
+def test_score_spikes(sattn, dev, shape):
+    T, hq, hkv = shape
+    note(f"score spikes T={T} Hq={hq} Hkv={hkv}")
+    x, (k1, k2) = spiked(T, hq, hkv, seed=22)
+    around = [k + d for k in (k1, k2) for d in (-1, 0, 1, 2, 31, 32, 63, 64)]
+    around += [(k2 // 64) * 64 + d for d in (0, 31, 32, 63)]
+    O, L = compare(sattn, dev, x, f"spikes T={T}", extra_rows=around)
+    # past the second spike the weights are all on it: O is that V row
+    G = hq // hkv
+    for h in range(hq):
+        v2 = x.Vt[h // G, :, k2].astype(np.float64)
+        assert np.abs(O[k2:, h * 64:(h + 1) * 64] - v2[None, :]).max() <= TOL_O
+
+
+@pytest.mark.parametrize("shape", [(4095, 32, 8), (8192, 16, 8), (8192, 16, 16)])
+def test_eight_wave_shapes(sattn, dev, shape):
+    T, hq, hkv = shape
+    note(f"eight-wave grid T={T} Hq={hq} Hkv={hkv}")
+    x = make_inputs(T, hq, hkv, seed=23, peaked_fraction=0.01)
+    compare(sattn, dev, x, f"T={T} Hq={hq} Hkv={hkv}")
