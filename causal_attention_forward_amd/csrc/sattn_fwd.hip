@@ -31,10 +31,12 @@
 //    matrix products reads its LDS operand four products ahead and is
 //    followed by the exponentials of two scores.  Two register sets of S and
 //    of binary16 P alternate between steps, so no copies carry them.
-//  * K tiles live in a 4-buffer LDS ring (tile t is read at steps t-1 and t),
-//    V^T tiles in a 3-buffer ring (read at step t+1); one barrier per step.
-//    Global loads run two steps ahead of their LDS stores through two
-//    register sets, and every step issues the same loads (tiles past the end
+//  * K tile t is read at steps t-1 and t, V^T tile t at step t+1.  With one
+//    workgroup per CU (NW = 8) two K and two V^T tiles are staged per barrier,
+//    every other step, into rings of 6 and 5 LDS buffers (101 KiB); with two
+//    workgroups per CU (NW = 4) one of each per step, into rings of 4 and 3.
+//    Global loads run one stage (two steps) ahead of their LDS stores through
+//    registers, and every stage issues the same loads (tiles past the end
 //    read as zeros through buffer-descriptor range checks), so the waits on
 //    them stay exact.  LDS rows are padded to 144 bytes so the 16-byte
 //    operand reads of 16 lanes hit 64 distinct banks.
@@ -135,8 +137,11 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
                  float c, int T, int Hq, int Hkv, int G, int nBlocks, int nPairs, int nSlotGroups,
                  int nHeadGroups) {
   constexpr int RS = NW / GW;              // row slots per workgroup
-  constexpr int kKRing = 4;                // K tile t is read at steps t-1 and t
-  constexpr int kVRing = 3;                // V^T tile t is read at step t+1
+  // With one workgroup per CU (NW = 8) two tiles are staged per barrier,
+  // which needs deeper rings (see the stage below).
+  constexpr bool kPair = NW == 8;
+  constexpr int kKRing = kPair ? 6 : 4;    // K tile t is read at steps t-1 and t
+  constexpr int kVRing = kPair ? 5 : 3;    // V^T tile t is read at step t+1
   constexpr float kSumCap = 256.0f;        // 2^kLazy
   constexpr int kOutOfRange = 0x7FFFFFF0;  // a buffer offset past every range
   __shared__ __attribute__((aligned(16))) half_t smem[(kKRing + kVRing) * kTileHalfs];
@@ -409,10 +414,11 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
     };
 
     // Ring schedule: K tile t is read at steps t-1 (S of t) and t (overflow
-    // fallback), V^T tile t at step t+1 (P V of t).  Stage j writes K of tile
-    // j+2 and V^T of tile j (loaded at stage j-2 into register set j % 2) into
-    // buffers last read at step j-2, then loads K of tile j+4 and V^T of tile
-    // j+2 into the same set; one barrier per step.
+    // fallback), V^T tile t at step t+1 (P V of t).  With NW = 4, stage j
+    // writes K of tile j+2 and V^T of tile j (loaded at stage j-2 into register
+    // set j % 2) into buffers last read at step j-2, then loads K of tile j+4
+    // and V^T of tile j+2 into the same set; one barrier per step.  With
+    // NW = 8, see the stage itself.
     Stage setK[2], setV[2];
     load_k(0, setK[0]);
     store_k(0, setK[0]);
@@ -429,12 +435,31 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
     // has no branches.
     auto stage = [&](auto PARF, int j) {
       constexpr int P = decltype(PARF)::value;
-      store_k((j + 2) % kKRing, setK[P]);
-      store_v(j % kVRing, setV[P]);
-      load_k(j + 4, setK[P]);
-      load_v(j + 2, setV[P]);
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      barrier();
+      if constexpr (kPair) {
+        // Even j only: K of tiles j+2, j+3 and V^T of tiles j, j+1 go into
+        // buffers whose tiles were last read at step j-3, before the previous
+        // barrier (j-2); other waves may still be in steps j-2, j-1, which read
+        // K of tiles j-2 .. j and V^T of tiles j-3, j-2 — other buffers.
+        if constexpr (P == 0) {
+          store_k((j + 2) % kKRing, setK[0]);
+          store_k((j + 3) % kKRing, setK[1]);
+          store_v(j % kVRing, setV[0]);
+          store_v((j + 1) % kVRing, setV[1]);
+          load_k(j + 4, setK[0]);
+          load_k(j + 5, setK[1]);
+          load_v(j + 2, setV[0]);
+          load_v(j + 3, setV[1]);
+          __builtin_amdgcn_s_waitcnt(0xC07F);
+          barrier();
+        }
+      } else {
+        store_k((j + 2) % kKRing, setK[P]);
+        store_v(j % kVRing, setV[P]);
+        load_k(j + 4, setK[P]);
+        load_v(j + 2, setV[P]);
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        barrier();
+      }
     };
     using T1 = std::integral_constant<bool, true>;
     using F0 = std::integral_constant<bool, false>;
