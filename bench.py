@@ -73,6 +73,58 @@ def cpu_baseline(x, budget_s=20.0):
                       f"({dt:.1f} s, float64 NumPy)"}
 
 
+def compulsory_bytes(T, Hq, Hkv, d=64):
+    """Q, K and V^T read once, O and L written once."""
+    return 2 * d * T * (Hq + 2 * Hkv) + 2 * d * T * Hq + 4 * T * Hq
+
+
+def sweep(torch, sattn, workloads, make_workload, reps=5, calls=50):
+    """Every synthetic workload: median over `reps` runs of `calls` back-to-back
+    launches, cycling through enough input/output sets (at least 4, about
+    300 MB in all, at most 64) that a small workload is not timed from cache."""
+    import math
+    import statistics
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    for idx, w in enumerate(workloads):
+        x = make_workload(idx)
+        nbytes = compulsory_bytes(x.T, x.Hq, x.Hkv)
+        nsets = min(64, max(4, math.ceil(300e6 / nbytes)))
+        sets = []
+        for _ in range(nsets):
+            sets.append((torch.from_numpy(x.Q).to(dev), torch.from_numpy(x.K).to(dev),
+                         torch.from_numpy(x.Vt).to(dev),
+                         torch.empty((x.T, x.Hq * 64), dtype=torch.float16, device=dev),
+                         torch.empty((x.Hq, x.T), dtype=torch.float32, device=dev)))
+
+        def call(i):
+            q, k, vt, O, L = sets[i % nsets]
+            sattn.fwd(q, k, vt, x.c, out=O, lse=L, stream=stream)
+
+        for i in range(max(200, 2 * nsets)):
+            call(i)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for i in range(calls):
+                call(i)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            times.append(ev0.elapsed_time(ev1) / calls)
+        ms = statistics.median(times)
+        tflops = causal_flops(x.T, x.Hq) / (ms * 1e-3) / 1e12
+        print(json.dumps({
+            "sweep": w.name, "T": x.T, "Hq": x.Hq, "Hkv": x.Hkv, "us_per_call": round(ms * 1e3, 2),
+            "tflops": round(tflops, 2), "pct_fp16_peak": round(100 * tflops / PEAK_FP16_TFLOPS, 2),
+            "compulsory_bytes": nbytes, "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "input_sets": nsets}), flush=True)
+        del sets
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -81,6 +133,9 @@ def main():
                     help="untimed calls first; the GPU needs a few tens of ms of load to reach its working clock")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the headline line, one JSON line per synthetic workload "
+                         "(median of 5 timed runs, input sets rotated so small ones are not cache figures)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the attention, run device-to-device copies of MIB MiB "
                          "(the reference transfer for scaling HBM byte counters)")
@@ -105,6 +160,10 @@ def main():
 
     from causal_attention_forward_amd import sattn
     from causal_attention_forward_amd.inputs import WORKLOADS, make_workload
+
+    if args.sweep:
+        sweep(torch, sattn, WORKLOADS, make_workload)
+        return
 
     w = WORKLOADS[WORKLOAD_INDEX]
     x = make_workload(WORKLOAD_INDEX)

@@ -420,14 +420,18 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
     // and V^T of tile j+2 into the same set; one barrier per step.  With
     // NW = 8, see the stage itself.
     Stage setK[2], setV[2];
-    load_k(0, setK[0]);
-    store_k(0, setK[0]);
-    load_k(1, setK[1]);
-    store_k(1, setK[1]);
-    load_k(2, setK[0]);
-    load_v(0, setV[0]);
-    load_k(3, setK[1]);
-    load_v(1, setV[1]);
+    {
+      // every load of the prologue in flight before the first store waits
+      Stage k0, k1;
+      load_k(0, k0);
+      load_k(1, k1);
+      load_k(2, setK[0]);
+      load_v(0, setV[0]);
+      load_k(3, setK[1]);
+      load_v(1, setV[1]);
+      store_k(0, k0);
+      store_k(1, k1);
+    }
     __builtin_amdgcn_s_waitcnt(0xC07F);
     barrier();
     // Loads past the last tile read zeros and stores of them land in ring
