@@ -92,3 +92,18 @@ def make_workload(index: int, seed: int | None = None) -> Inputs:
     return make_inputs(w.T, w.Hq, w.Hkv, index if seed is None else seed,
                        qk_std=w.qk_std, v_std=w.v_std,
                        peaked_fraction=w.peaked_fraction, peak_offset=w.peak_offset)
+
+
+def make_output_gradient(T: int, Hq: int, seed: int, *, std: float = 1.0) -> np.ndarray:
+    """The output gradient dO for the backward: binary16, token-major
+    ``[T][Hq*64]`` like the forward's O (element (i, h, d) at i*Hq*64 + h*64 + d).
+
+    Recipe: ``numpy.random.default_rng([seed, 68])`` (a stream separate from
+    the one ``make_inputs`` draws Q, K, V from for the same seed); float32
+    standard normals of shape ``[T][Hq*64]`` times ``std``, rounded to binary16.
+    """
+    if T < 0 or Hq < 1:
+        raise ValueError("need T >= 0, Hq >= 1")
+    rng = np.random.default_rng([seed, 68])
+    g = rng.standard_normal((T, Hq * HEAD_DIM), dtype=np.float32) * np.float32(std)
+    return np.ascontiguousarray(g.astype(np.float16))
