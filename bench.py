@@ -1,10 +1,15 @@
-"""Benchmark of the causal streaming-attention forward on one MI355X.
+"""Benchmark of causal streaming attention on one MI355X.
 
 One step = one sattn_fwd call over the T=4096, Hq=32, Hkv=8, d=64 workload
 (seeded synthetic fp16 inputs, already resident in HBM).  Prints one JSON
 line: causal TFLOP/s (4*T^2*64*Hq/2 flop per call), the roofline of the
 kernel against the fp16 dense MFMA peak, and the float64 CPU oracle timed on
 a bounded sample of the same workload.
+
+With --backward, one step is one sattn_bwd call (query launch, key launch,
+grouped reduction) on the same workload, with dO seeded and O and L from the
+forward; its line counts the five products S, dP, dQ, dK, dV once each
+(2.5 x the forward's flop) and gives each launch's own time.
 """
 import argparse
 import hashlib
@@ -73,6 +78,133 @@ def cpu_baseline(x, budget_s=20.0):
                       f"({dt:.1f} s, float64 NumPy)"}
 
 
+def backward_flops(T, Hq, d=64):
+    """S, dP, dQ, dK and dV, each 2*64 flop per causal (query, key) pair."""
+    return 2.5 * causal_flops(T, Hq, d)
+
+
+def cpu_baseline_backward(x, dO, O, L, s, budget_s=20.0):
+    """The float64 backward oracle on whole query heads (each with its own
+    K/V head), as many as fit in about budget_s seconds, scaled to TFLOP/s."""
+    from oracle import attention_backward_ref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    G = x.Hq // x.Hkv
+    t0 = time.perf_counter()
+    heads = 0
+    while heads < x.Hq:
+        h, kv = heads, heads // G
+        cols = slice(h * 64, (h + 1) * 64)
+        attention_backward_ref(x.Q[h:h + 1], x.K[kv:kv + 1], x.Vt[kv:kv + 1], O[:, cols],
+                               dO[:, cols], L[h:h + 1], x.c, s)
+        heads += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = backward_flops(x.T, 1) * heads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"backward of {heads} of {x.Hq} query heads of T={x.T} Hq={x.Hq} "
+                      f"Hkv={x.Hkv} ({dt:.1f} s, float64 NumPy)"}
+
+
+def bench_backward(args, torch, sattn, x, w):
+    """The --backward line (see the module docstring)."""
+    import numpy as np
+    from causal_attention_forward_amd.inputs import make_output_gradient
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(x.Q).to(dev)
+    k = torch.from_numpy(x.K).to(dev)
+    vt = torch.from_numpy(x.Vt).to(dev)
+    dO_np = make_output_gradient(x.T, x.Hq, WORKLOAD_INDEX)
+    do = torch.from_numpy(dO_np).to(dev)
+    O, L = sattn.fwd(q, k, vt, x.c)
+    T, Hq, Hkv = x.T, x.Hq, x.Hkv
+    s = 0.125
+    f32 = dict(dtype=torch.float32, device=dev)
+    dQ, D = torch.empty((Hq, T, 64), **f32), torch.empty((Hq, T), **f32)
+    dK, dVt = torch.empty((Hkv, T, 64), **f32), torch.empty((Hkv, 64, T), **f32)
+    need = sattn.sattn_bwd_workspace_bytes(T, Hq, Hkv)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    ptr = lambda t: t.data_ptr()  # noqa: E731
+
+    def query():
+        st = sattn.sattn_bwd_query(ptr(q), ptr(k), ptr(vt), ptr(O), ptr(do), ptr(L), ptr(dQ),
+                                   ptr(D), x.c, s, T, Hq, Hkv, sp)
+        assert st == sattn.SATTN_OK, st
+
+    def key():
+        st = sattn.sattn_bwd_key(ptr(q), ptr(k), ptr(vt), ptr(do), ptr(L), ptr(D), ptr(dK),
+                                 ptr(dVt), ptr(ws), need, x.c, s, T, Hq, Hkv, sp)
+        assert st == sattn.SATTN_OK, st
+
+    def step():
+        st = sattn.sattn_bwd(ptr(q), ptr(k), ptr(vt), ptr(O), ptr(do), ptr(L), ptr(dQ), ptr(dK),
+                             ptr(dVt), ptr(D), ptr(ws), need, x.c, s, T, Hq, Hkv, sp)
+        assert st == sattn.SATTN_OK, st
+
+    def timed(fn, n):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(n):
+            fn()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    n_each = max(args.steps // 2, 1)
+    query_ms = timed(query, n_each)
+    key_ms = timed(key, n_each)
+
+    flops = backward_flops(T, Hq)
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    key_flops = 2.0 * causal_flops(T, Hq)      # S, dP, dV, dK
+    query_flops = 1.5 * causal_flops(T, Hq)    # S, dP, dQ
+    key_tf = key_flops / (key_ms * 1e-3) / 1e12
+    out = {
+        "metric": "causal attn bwd TFLOP/s (S, dP, dQ, dK, dV = 2.5x fwd flop), T=4096 Hq=32 Hkv=8 d=64",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": w.name + " backward", "T": T, "Hq": Hq, "Hkv": Hkv,
+                   "head_dim": 64, "causal": True, "flop_per_call": flops,
+                   "query_launch_ms": round(query_ms, 5),
+                   "query_launch_tflops": round(query_flops / (query_ms * 1e-3) / 1e12, 2),
+                   "key_launch_and_reduction_ms": round(key_ms, 5)},
+        "roofline": {"bound": "mfma", "achieved": round(key_tf, 2), "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(key_tf / PEAK_FP16_TFLOPS, 4),
+                     "traffic": None, "kernel": "key launch + reduction (4 products)",
+                     "kernel_ms": round(key_ms, 5)},
+    }
+    if not args.no_cpu_baseline:
+        O_np = O.cpu().numpy()
+        L_np = L.cpu().numpy()
+        out["cpu_baseline"] = cpu_baseline_backward(x, dO_np, O_np, L_np, s, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
 def compulsory_bytes(T, Hq, Hkv, d=64):
     """Q, K and V^T read once, O and L written once."""
     return 2 * d * T * (Hq + 2 * Hkv) + 2 * d * T * Hq + 4 * T * Hq
@@ -136,6 +268,8 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline line, one JSON line per synthetic workload "
                          "(median of 5 timed runs, input sets rotated so small ones are not cache figures)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (sattn_bwd) instead of the forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the attention, run device-to-device copies of MIB MiB "
                          "(the reference transfer for scaling HBM byte counters)")
@@ -167,6 +301,9 @@ def main():
 
     w = WORKLOADS[WORKLOAD_INDEX]
     x = make_workload(WORKLOAD_INDEX)
+    if args.backward:
+        bench_backward(args, torch, sattn, x, w)
+        return
     dev = torch.device("cuda:0")
     q = torch.from_numpy(x.Q).to(dev)
     k = torch.from_numpy(x.K).to(dev)

@@ -50,6 +50,116 @@ extern "C" int sattn_fwd_check(const void* Q, const void* K, const void* Vt, con
   return SATTN_OK;
 }
 
+namespace {
+
+int check_shape_scale(float c, int T, int Hq, int Hkv) {
+  if (T < 1 || Hq < 1 || Hkv < 1) return SATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0 || Hq > 65535) return SATTN_ERR_SHAPE;
+  if (static_cast<uint64_t>(Hq) * SATTN_HEAD_DIM * static_cast<uint64_t>(T) * 4u > 0xFFFFFFFFull)
+    return SATTN_ERR_SHAPE;
+  if (!isfinite(c) || !(c > 0.0f)) return SATTN_ERR_SCALE;
+  return SATTN_OK;
+}
+
+bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+// The argument set of one backward launch; absent pointers are NULL and
+// `need` says which of them the launch requires.
+struct BwdArgs {
+  const void *Q, *K, *Vt, *O, *dO, *L;      // inputs
+  const void *dQ, *D_out, *dK, *dVt, *ws;   // outputs (D is an input of the key launch)
+  const void* D_in;
+  unsigned long long wsBytes;
+  float c, s;
+  int T, Hq, Hkv;
+};
+
+int check_bwd(const BwdArgs& a, bool query, bool key) {
+  if (!a.Q || !a.K || !a.Vt || !a.dO || !a.L) return SATTN_ERR_NULL;
+  if (query && (!a.O || !a.dQ || !a.D_out)) return SATTN_ERR_NULL;
+  if (key && (!a.dK || !a.dVt)) return SATTN_ERR_NULL;
+  if (key && !query && !a.D_in) return SATTN_ERR_NULL;
+  int st = check_shape_scale(a.c, a.T, a.Hq, a.Hkv);
+  if (st != SATTN_OK) return st;
+  if (!isfinite(a.s) || !(a.s > 0.0f)) return SATTN_ERR_SCALE;
+  const unsigned long long need = sattn_bwd_workspace_bytes(a.T, a.Hq, a.Hkv);
+  if (key && need > 0 && (!a.ws || a.wsBytes < need)) return SATTN_ERR_WORKSPACE;
+  if (misaligned(a.Q, 16) || misaligned(a.K, 16) || misaligned(a.Vt, 16) ||
+      misaligned(a.dO, 16) || misaligned(a.L, 4))
+    return SATTN_ERR_ALIGN;
+  if (query && (misaligned(a.O, 16) || misaligned(a.dQ, 16) || misaligned(a.D_out, 4)))
+    return SATTN_ERR_ALIGN;
+  if (key && (misaligned(a.dK, 16) || misaligned(a.dVt, 16) || misaligned(a.ws, 16) ||
+              misaligned(a.D_in, 4)))
+    return SATTN_ERR_ALIGN;
+  const uint64_t t = static_cast<uint64_t>(a.T);
+  const uint64_t hq = static_cast<uint64_t>(a.Hq), hkv = static_cast<uint64_t>(a.Hkv);
+  const uint64_t half = t * SATTN_HEAD_DIM * 2u, word = t * SATTN_HEAD_DIM * 4u;
+  Span in[7];
+  int nIn = 0;
+  in[nIn++] = span(a.Q, hq * half);
+  in[nIn++] = span(a.K, hkv * half);
+  in[nIn++] = span(a.Vt, hkv * half);
+  in[nIn++] = span(a.dO, hq * half);
+  in[nIn++] = span(a.L, hq * t * 4u);
+  if (query) in[nIn++] = span(a.O, hq * half);
+  if (key && !query) in[nIn++] = span(a.D_in, hq * t * 4u);
+  Span out[5];
+  int nOut = 0;
+  if (query) {
+    out[nOut++] = span(a.dQ, hq * word);
+    out[nOut++] = span(a.D_out, hq * t * 4u);
+  }
+  if (key) {
+    out[nOut++] = span(a.dK, hkv * word);
+    out[nOut++] = span(a.dVt, hkv * word);
+    if (need > 0) out[nOut++] = span(a.ws, need);
+  }
+  for (int i = 0; i < nOut; ++i) {
+    for (int j = 0; j < nIn; ++j)
+      if (overlaps(out[i], in[j])) return SATTN_ERR_ALIAS;
+    for (int j = i + 1; j < nOut; ++j)
+      if (overlaps(out[i], out[j])) return SATTN_ERR_ALIAS;
+  }
+  return SATTN_OK;
+}
+
+}  // namespace
+
+extern "C" unsigned long long sattn_bwd_workspace_bytes(int T, int Hq, int Hkv) {
+  if (check_shape_scale(1.0f, T, Hq, Hkv) != SATTN_OK || Hq == Hkv) return 0;
+  return 2ull * static_cast<unsigned long long>(Hq) * static_cast<unsigned long long>(T) *
+         SATTN_HEAD_DIM * 4ull;
+}
+
+extern "C" int sattn_bwd_check(const void* Q, const void* K, const void* Vt, const void* O,
+                               const void* dO, const float* L, const float* dQ, const float* dK,
+                               const float* dVt, const float* D, const void* workspace,
+                               unsigned long long workspace_bytes, float c, float s, int T,
+                               int Hq, int Hkv) {
+  const BwdArgs a{Q, K, Vt, O, dO, L, dQ, D, dK, dVt, workspace, nullptr, workspace_bytes,
+                  c, s, T, Hq, Hkv};
+  return check_bwd(a, true, true);
+}
+
+extern "C" int sattn_bwd_query_check(const void* Q, const void* K, const void* Vt, const void* O,
+                                     const void* dO, const float* L, const float* dQ,
+                                     const float* D, float c, float s, int T, int Hq, int Hkv) {
+  const BwdArgs a{Q, K, Vt, O, dO, L, dQ, D, nullptr, nullptr, nullptr, nullptr, 0,
+                  c, s, T, Hq, Hkv};
+  return check_bwd(a, true, false);
+}
+
+extern "C" int sattn_bwd_key_check(const void* Q, const void* K, const void* Vt, const void* dO,
+                                   const float* L, const float* D, const float* dK,
+                                   const float* dVt, const void* workspace,
+                                   unsigned long long workspace_bytes, float c, float s, int T,
+                                   int Hq, int Hkv) {
+  const BwdArgs a{Q, K, Vt, nullptr, dO, L, nullptr, nullptr, dK, dVt, workspace, D,
+                  workspace_bytes, c, s, T, Hq, Hkv};
+  return check_bwd(a, false, true);
+}
+
 extern "C" const char* sattn_status_string(int status) {
   switch (status) {
     case SATTN_OK: return "ok";
@@ -57,11 +167,14 @@ extern "C" const char* sattn_status_string(int status) {
     case SATTN_ERR_SHAPE:
       return "bad shape: need T >= 1, Hq >= 1, Hkv >= 1, Hq % Hkv == 0, Hq <= 65535 and "
              "Hq*64*T*4 <= 2^32-1";
-    case SATTN_ERR_SCALE: return "the scale c must be finite and > 0";
-    case SATTN_ERR_ALIGN: return "Q, K, Vt and O must be 16-byte aligned and L 4-byte aligned";
-    case SATTN_ERR_ALIAS: return "O or L overlaps an input or each other";
+    case SATTN_ERR_SCALE: return "the scales c and s must be finite and > 0";
+    case SATTN_ERR_ALIGN:
+      return "binary16 arrays, dQ, dK, dVt and the workspace must be 16-byte aligned, L and D "
+             "4-byte aligned";
+    case SATTN_ERR_ALIAS: return "an output overlaps an input or another output";
     case SATTN_ERR_DEVICE: return "no current HIP device, or it is not gfx950";
     case SATTN_ERR_LAUNCH: return "the kernel launch failed";
+    case SATTN_ERR_WORKSPACE: return "the workspace is NULL or smaller than sattn_bwd_workspace_bytes()";
     default: return "unknown sattn status";
   }
 }

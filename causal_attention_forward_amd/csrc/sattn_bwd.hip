@@ -1,0 +1,577 @@
+// The backward of causal streaming attention for gfx950 (CDNA4): the query
+// launch (row term D and dQ), the key launch (dK and dV^T, one plane per
+// query head) and the grouped gradient reduction, with their C entries.
+//
+// Method (StreamingAttentionSM86 page: the comment opening the backward pass
+// and those of its query launch, key launch and grouped reduction): P is
+// recomputed from the forward's base-2 log-sum-exp, P = 2^(S c - L); with
+// dP = dO V^T and D = rowsum(dO * O), dS = P (dP - D); then dQ = s dS K,
+// dK = s dS^T Q and dV = P^T dO.  The query launch walks the key tiles up to
+// its rows' diagonal keeping dQ; the key launch walks the query tiles from
+// its keys' diagonal to the end keeping dK and dV.  S and dP are formed in
+// both launches, so neither needs the other's partial sums: there are no
+// atomics, and every sum is taken in a fixed order.  P and dS are rounded to
+// binary16 as operands of the products that follow (P for dV, dS for dQ and
+// dK); all accumulation is binary32.
+//
+// gfx950 design (not the page's SM86 one):
+//  * Products run on v_mfma_f32_32x32x16_f16.  Its two operands take, per
+//    lane, eight consecutive elements along the contraction, and its
+//    accumulator gives a lane one column and 16 rows.  Each launch picks the
+//    orientation whose accumulator feeds the next product directly: the
+//    query launch forms S^T and dP^T (a lane holds one query, so L and D are
+//    per-lane constants) and the key launch S and dP (a lane holds one key).
+//    The row order of the natural operand is permuted (krow) so that the
+//    accumulator's 16 rows per lane are the 2 x 8 consecutive indices the
+//    following product contracts over.
+//  * Operands that the products need along the other axis of a tile staged
+//    in LDS (K^T and V rows from the V^T tile in the query launch; Q^T and
+//    dO^T in the key launch) are read with ds_read_b64_tr_b16, the LDS
+//    transpose read: a 16-lane group whose lanes point at four rows of a
+//    16-column block receives that block transposed, four consecutive rows
+//    per lane.  Two such reads make one operand, so the backward consumes the
+//    forward's own layouts (Q, K, V^T, token-major O) and no transposed copy
+//    of anything is written to memory.
+//  * A wave owns 32 queries (query launch) or 32 keys (key launch); a
+//    workgroup is four waves on consecutive rows and stages each 64-row tile
+//    once for all of them, double-buffered.  Workgroups are issued heaviest
+//    first.
+//  * With GQA the key launch writes one dK and one dV^T plane per query head
+//    into a caller-provided workspace and a reduction sums the G planes of
+//    each K/V head in head order; with Hq == Hkv it writes dK and dV^T
+//    directly.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "sattn.h"
+
+namespace {
+
+typedef _Float16 half_t;
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+constexpr int kD = SATTN_HEAD_DIM;              // head width
+constexpr int kTile = 64;                       // rows of a staged K, V^T, Q or dO tile
+constexpr int kRowHalfs = kD + 8;               // LDS row: 64 values + 16 bytes of padding
+constexpr int kTileHalfs = kTile * kRowHalfs;
+constexpr int kBufferWord3 = 0x00020000;        // raw buffer, 32-bit data format
+constexpr int kOutOfRange = 0x7FFFFFF0;         // a buffer offset past every range
+constexpr int kNW = 4;                          // waves per workgroup
+
+__device__ __forceinline__ float16v mfma(half8 a, half8 b, float16v c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// The value held by the lane whose byte address (lane index * 4) is `addr`.
+__device__ __forceinline__ float xlane(float x, int addr) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, x)));
+}
+
+// Row of the natural operand loaded by operand row m, chosen so that
+// accumulator element i of lane (n, g) is index 16*(i/8) + 8g + i%8 of the
+// 32-row block: bits 2 and 3 of m swapped.
+__device__ __forceinline__ int krow(int m) {
+  const int a = m >> 3, e = (m >> 2) & 1, b = m & 3;
+  return 16 * (a >> 1) + 8 * e + 4 * (a & 1) + b;
+}
+
+__device__ __forceinline__ half8 ld8(const half_t* p) { return *reinterpret_cast<const half8*>(p); }
+
+// ds_read_b64_tr_b16 at p: within each 16-lane group, lane 4a + b supplies
+// the address of row a, columns 4b'..4b'+3 of a block, and lane t receives
+// rows 0..3 of the column that lanes 4(t/4)'s supplier pointed at, offset t%4.
+__device__ __forceinline__ half4 lds_tr4(const half_t* p) {
+  typedef __attribute__((address_space(3))) short4v lds_short4;
+  const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(const_cast<half_t*>(p)));
+  return __builtin_bit_cast(half4, v);
+}
+
+// Operand whose lane l holds X[m][k0 + 8(l/32) .. +7] for a tile stored
+// k-major in LDS (X[m][k] at row k, column m): two transpose reads, rows
+// k .. k+3 and k+4 .. k+7.  `p` already includes the lane's own offset.
+__device__ __forceinline__ half8 tr8(const half_t* p) {
+  const half4 lo = lds_tr4(p), hi = lds_tr4(p + 4 * kRowHalfs);
+  return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// A lane's offset (halfs) for tr8 over a k-major tile: row 8(l/32) + (l%16)/4,
+// column 16((l/16)%2) + 4 c(l%4), where c is the identity (the operand's row m
+// is l%32) or swaps the two bits of l%4 (its row m is krow(l%32)).
+__device__ __forceinline__ int tr_offset(int lane, bool permuted) {
+  const int b = lane & 3;
+  const int cb = permuted ? (((b & 1) << 1) | (b >> 1)) : b;
+  return (8 * (lane >> 5) + ((lane & 15) >> 2)) * kRowHalfs + 16 * ((lane >> 4) & 1) + 4 * cb;
+}
+
+// binary16 operand of 16 consecutive indices from accumulator elements
+// 8h .. 8h+7 (round to nearest even).
+__device__ __forceinline__ half8 pack8(const float16v& x, int h) {
+  half8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (half_t)x[8 * h + e];
+  return r;
+}
+
+// -------------------------------------------------------------------------
+// Query launch: D and dQ.  Workgroup = kNW waves x 32 query rows of head h.
+// -------------------------------------------------------------------------
+template <bool VT_VEC>
+__global__ void __launch_bounds__(64 * kNW, 2)
+sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
+                  const half_t* __restrict__ Vt, const half_t* __restrict__ O,
+                  const half_t* __restrict__ dO, const float* __restrict__ L,
+                  float* __restrict__ dQ, float* __restrict__ D, float c, float s, int T, int Hq,
+                  int G, int nBlocks) {
+  __shared__ __attribute__((aligned(16))) half_t smem[4 * kTileHalfs];
+  half_t* const kbuf = smem;                   // K tiles [2][64 keys][72]
+  half_t* const vbuf = smem + 2 * kTileHalfs;  // V^T tiles [2][64 d][72]
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 31;
+  const int g = lane >> 5;
+
+  const int blk = nBlocks - 1 - (int)blockIdx.x / Hq;  // heaviest first
+  const int h = (int)blockIdx.x % Hq;
+  const int kv = h / G;
+  const int row0 = blk * 32 * kNW;
+  const int waveRow0 = row0 + 32 * wave;
+  const int row = waveRow0 + n;
+  const bool live = row < T;
+  const int nkt = min(T - 1, row0 + 32 * kNW - 1) / kTile + 1;  // key tiles of the workgroup
+  const int waveLast = min(T - 1, waveRow0 + 31);               // the wave's last row
+
+  // Q and dO rows as B operands (lane: row n, columns 16kk + 8g .. +7), and D.
+  half8 qf[4], dof[4];
+  float dpart = 0.0f;
+  {
+    const half_t* qrow = Q + ((size_t)h * T + row) * kD + 8 * g;
+    const size_t tok = (size_t)row * Hq * kD + (size_t)h * kD + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const half8 z = {};
+      qf[kk] = live ? ld8(qrow + 16 * kk) : z;
+      dof[kk] = live ? *reinterpret_cast<const half8*>(dO + tok + 16 * kk) : z;
+      const half8 of = live ? *reinterpret_cast<const half8*>(O + tok + 16 * kk) : z;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dpart = fmaf((float)dof[kk][e], (float)of[e], dpart);
+    }
+  }
+  const float Drow = dpart + xlane(dpart, (lane ^ 32) << 2);
+  const float negL = live ? -L[(size_t)h * T + row] : 0.0f;
+  if (live && g == 0) D[(size_t)h * T + row] = Drow;
+
+  // Staging: thread t owns 16-byte chunks t and t + 256 of a K tile (row
+  // c/8, column chunk c%8) and of a V^T tile.
+  const int cr = tid >> 3, cc = tid & 7;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<half_t*>(K + (size_t)kv * T * kD), 0, T * kD * 2, kBufferWord3);
+  const half_t* Vh = Vt + (size_t)kv * kD * T;
+  const __amdgpu_buffer_rsrc_t vrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(Vh), 0, kD * T * 2, kBufferWord3);
+  int4v kst[2], vst[2];
+  auto load = [&](int kt) {
+    const int key0 = kt * kTile;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int r = cr + 32 * p;
+      kst[p] = __builtin_amdgcn_raw_buffer_load_b128(krsrc, ((key0 + r) * kD + cc * 8) * 2, 0, 0);
+      if (VT_VEC) {
+        const int off = key0 + cc * 8 < T ? (r * T + key0 + cc * 8) * 2 : kOutOfRange;
+        vst[p] = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off, 0, 0);
+      } else {
+        half8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = key0 + cc * 8 + e;
+          v[e] = key < T ? Vh[(size_t)r * T + key] : (half_t)0;
+        }
+        vst[p] = __builtin_bit_cast(int4v, v);
+      }
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int off = buf * kTileHalfs + (cr + 32 * p) * kRowHalfs + cc * 8;
+      *reinterpret_cast<int4v*>(kbuf + off) = kst[p];
+      *reinterpret_cast<int4v*>(vbuf + off) = vst[p];
+    }
+  };
+
+  const int kOff = krow(n) * kRowHalfs + 8 * g;  // natural K rows for S^T (keys krow(n))
+  const int vtOff = tr_offset(lane, true);      // V rows (keys krow(n)) from the V^T tile
+  const int ktOff = tr_offset(lane, false);     // K^T rows (d = n) from the K tile
+
+  float16v dq0 = {}, dq1 = {};
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nkt) load(kt + 1);
+    if (kt * kTile <= waveLast) {
+      const half_t* kb = kbuf + buf * kTileHalfs;
+      const half_t* vb = vbuf + buf * kTileHalfs;
+      // S^T = K Q^T and dP^T = V dO^T: keys 0..31 (x0) and 32..63 (x1) of the tile
+      float16v s0, s1, p0, p1;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const half8 a0 = ld8(kb + kOff + 16 * kk);
+        const half8 a1 = ld8(kb + kOff + 32 * kRowHalfs + 16 * kk);
+        s0 = mfma(a0, qf[kk], kk == 0 ? float16v{} : s0);
+        s1 = mfma(a1, qf[kk], kk == 0 ? float16v{} : s1);
+        const half8 v0 = tr8(vb + vtOff + 16 * kk * kRowHalfs);
+        const half8 v1 = tr8(vb + vtOff + 16 * kk * kRowHalfs + 32);
+        p0 = mfma(v0, dof[kk], kk == 0 ? float16v{} : p0);
+        p1 = mfma(v1, dof[kk], kk == 0 ? float16v{} : p1);
+      }
+      // the diagonal: key 64kt + 16(i/8) + 8g + i%8 (+32) is kept iff <= row
+      if (kt * kTile + kTile - 1 > waveRow0) {
+        const int lim = row - kt * kTile - 8 * g;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int k = 16 * (i >> 3) + (i & 7);
+          if (k > lim) s0[i] = -INFINITY;
+          if (k + 32 > lim) s1[i] = -INFINITY;
+        }
+      }
+      // P^T = 2^(S^T c - L), dS^T = P^T (dP^T - D)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c, negL)) * (p0[i] - Drow);
+        s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c, negL)) * (p1[i] - Drow);
+      }
+      const half8 ds[4] = {pack8(s0, 0), pack8(s0, 1), pack8(s1, 0), pack8(s1, 1)};
+      // dQ^T += K^T dS^T: d = n (dq0) and 32 + n (dq1), keys 16ck + 8g .. +7
+#pragma unroll
+      for (int ck = 0; ck < 4; ++ck) {
+        const half8 k0 = tr8(kb + ktOff + 16 * ck * kRowHalfs);
+        const half8 k1 = tr8(kb + ktOff + 16 * ck * kRowHalfs + 32);
+        dq0 = mfma(k0, ds[ck], dq0);
+        dq1 = mfma(k1, ds[ck], dq1);
+      }
+    }
+    if (kt + 1 < nkt) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // dQ = s * sum: accumulator element 4q + e of lane (n, g) is d = 8q + 4g + e
+  if (live) {
+    float* out = dQ + ((size_t)h * T + row) * kD + 4 * g;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4v a = {dq0[4 * q], dq0[4 * q + 1], dq0[4 * q + 2], dq0[4 * q + 3]};
+      const float4v b = {dq1[4 * q], dq1[4 * q + 1], dq1[4 * q + 2], dq1[4 * q + 3]};
+      *reinterpret_cast<float4v*>(out + 8 * q) = a * s;
+      *reinterpret_cast<float4v*>(out + 32 + 8 * q) = b * s;
+    }
+  }
+}
+
+// -------------------------------------------------------------------------
+// Key launch: dK and dV^T of query head h's contribution.  Workgroup = kNW
+// waves x 32 keys of K/V head h / G.
+// -------------------------------------------------------------------------
+template <bool VT_VEC>
+__global__ void __launch_bounds__(64 * kNW, 2)
+sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
+                  const half_t* __restrict__ Vt, const half_t* __restrict__ dO,
+                  const float* __restrict__ L, const float* __restrict__ D,
+                  float* __restrict__ dKp, float* __restrict__ dVp, float c, float s, int T,
+                  int Hq, int G) {
+  __shared__ __attribute__((aligned(16))) half_t smem[4 * kTileHalfs];
+  __shared__ __attribute__((aligned(16))) float rowterms[2][2][kTile];  // [buf][L, D][query]
+  half_t* const qbuf = smem;                    // Q tiles [2][64 queries][72]
+  half_t* const obuf = smem + 2 * kTileHalfs;   // dO tiles [2][64 queries][72]
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 31;
+  const int g = lane >> 5;
+
+  const int blk = (int)blockIdx.x / Hq;  // key block 0 has the most queries: heaviest first
+  const int h = (int)blockIdx.x % Hq;
+  const int kv = h / G;
+  const int key0 = blk * 32 * kNW;
+  const int waveKey0 = key0 + 32 * wave;
+  const int key = waveKey0 + n;
+  const bool live = key < T;
+  const int ft = key0 / kTile;                  // first query tile (key0 is a multiple of 64)
+  const int nt = (T + kTile - 1) / kTile;
+
+  // K and V rows of the wave's keys as B operands (lane: key n, d = 16kk + 8g .. +7)
+  half8 kf[4], vf[4];
+  {
+    const half_t* krow_p = K + ((size_t)kv * T + key) * kD + 8 * g;
+    const half_t* vcol = Vt + (size_t)kv * kD * T + key;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      kf[kk] = live ? ld8(krow_p + 16 * kk) : half8{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vf[kk][e] = live ? vcol[(size_t)(16 * kk + 8 * g + e) * T] : (half_t)0;
+    }
+  }
+
+  // Staging: thread t owns 16-byte chunks t and t + 256 of the Q tile and of
+  // the dO tile (row c/8, column chunk c%8); threads 0..63 the tile's L and
+  // threads 64..127 its D (rows past T read L = +inf and D = 0, so P = 0).
+  const int cr = tid >> 3, cc = tid & 7;
+  const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<half_t*>(Q + (size_t)h * T * kD), 0, T * kD * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<half_t*>(dO + (size_t)h * kD), 0, (T * Hq - h) * kD * 2, kBufferWord3);
+  int4v qst[2], ost[2];
+  float rst = 0.0f;
+  auto load = [&](int it) {
+    const int q0 = it * kTile;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int r = q0 + cr + 32 * p;
+      qst[p] = __builtin_amdgcn_raw_buffer_load_b128(qrsrc, (r * kD + cc * 8) * 2, 0, 0);
+      ost[p] = __builtin_amdgcn_raw_buffer_load_b128(
+          orsrc, (int)(((unsigned)r * (unsigned)Hq * kD + cc * 8) * 2u), 0, 0);
+    }
+    if (tid < 2 * kTile) {
+      const int q = q0 + (tid & (kTile - 1));
+      const bool isL = tid < kTile;
+      rst = q < T ? (isL ? L : D)[(size_t)h * T + q] : (isL ? INFINITY : 0.0f);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int off = buf * kTileHalfs + (cr + 32 * p) * kRowHalfs + cc * 8;
+      *reinterpret_cast<int4v*>(qbuf + off) = qst[p];
+      *reinterpret_cast<int4v*>(obuf + off) = ost[p];
+    }
+    if (tid < 2 * kTile) rowterms[buf][tid >> 6][tid & (kTile - 1)] = rst;
+  };
+
+  const int nOff = krow(n) * kRowHalfs + 8 * g;  // natural Q / dO rows (queries krow(n))
+  const int tOff = tr_offset(lane, false);       // Q^T / dO^T rows (d = n)
+
+  float16v dk0 = {}, dk1 = {}, dv0 = {}, dv1 = {};
+  load(ft);
+  store(0);
+  __syncthreads();
+  for (int it = ft; it < nt; ++it) {
+    const int buf = (it - ft) & 1;
+    if (it + 1 < nt) load(it + 1);
+    if (it * kTile + kTile - 1 >= waveKey0) {
+      const half_t* qb = qbuf + buf * kTileHalfs;
+      const half_t* ob = obuf + buf * kTileHalfs;
+      // S = Q K^T and dP = dO V^T: queries 0..31 (x0) and 32..63 (x1) of the tile
+      float16v s0, s1, p0, p1;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const half8 a0 = ld8(qb + nOff + 16 * kk);
+        const half8 a1 = ld8(qb + nOff + 32 * kRowHalfs + 16 * kk);
+        s0 = mfma(a0, kf[kk], kk == 0 ? float16v{} : s0);
+        s1 = mfma(a1, kf[kk], kk == 0 ? float16v{} : s1);
+        const half8 b0 = ld8(ob + nOff + 16 * kk);
+        const half8 b1 = ld8(ob + nOff + 32 * kRowHalfs + 16 * kk);
+        p0 = mfma(b0, vf[kk], kk == 0 ? float16v{} : p0);
+        p1 = mfma(b1, vf[kk], kk == 0 ? float16v{} : p1);
+      }
+      // the diagonal: query 64it + 16(i/8) + 8g + i%8 (+32) is kept iff >= key
+      if (it * kTile < waveKey0 + 31) {
+        const int lim = key - it * kTile - 8 * g;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = 16 * (i >> 3) + (i & 7);
+          if (q < lim) s0[i] = -INFINITY;
+          if (q + 32 < lim) s1[i] = -INFINITY;
+        }
+      }
+      // P = 2^(S c - L) and dS = P (dP - D), eight queries at a time: block
+      // b holds queries 16b + 8g .. +7 of the tile (elements 8(b%2) .. of x(b/2))
+      const float* lt = rowterms[buf][0];
+      const float* dt = rowterms[buf][1];
+      half8 pb[4], db[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int q = 16 * b + 8 * g;
+        const float4v l0 = *reinterpret_cast<const float4v*>(lt + q);
+        const float4v l1 = *reinterpret_cast<const float4v*>(lt + q + 4);
+        const float4v d0 = *reinterpret_cast<const float4v*>(dt + q);
+        const float4v d1 = *reinterpret_cast<const float4v*>(dt + q + 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 8 * (b & 1) + e;
+          const float sv = b < 2 ? s0[i] : s1[i];
+          const float pv = b < 2 ? p0[i] : p1[i];
+          const float lv = e < 4 ? l0[e] : l1[e - 4];
+          const float dv = e < 4 ? d0[e] : d1[e - 4];
+          const float P = __builtin_amdgcn_exp2f(fmaf(sv, c, -lv));
+          pb[b][e] = (half_t)P;
+          db[b][e] = (half_t)(P * (pv - dv));
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS: d = n (x0) and 32 + n (x1),
+      // queries 16ck + 8g .. +7
+#pragma unroll
+      for (int ck = 0; ck < 4; ++ck) {
+        const half8 o0 = tr8(ob + tOff + 16 * ck * kRowHalfs);
+        const half8 o1 = tr8(ob + tOff + 16 * ck * kRowHalfs + 32);
+        dv0 = mfma(o0, pb[ck], dv0);
+        dv1 = mfma(o1, pb[ck], dv1);
+        const half8 q0 = tr8(qb + tOff + 16 * ck * kRowHalfs);
+        const half8 q1 = tr8(qb + tOff + 16 * ck * kRowHalfs + 32);
+        dk0 = mfma(q0, db[ck], dk0);
+        dk1 = mfma(q1, db[ck], dk1);
+      }
+    }
+    if (it + 1 < nt) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // accumulator element 4q + e of lane (n, g) is d = 8q + 4g + e of key n
+  if (live) {
+    float* kout = dKp + ((size_t)h * T + key) * kD + 4 * g;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4v a = {dk0[4 * q], dk0[4 * q + 1], dk0[4 * q + 2], dk0[4 * q + 3]};
+      const float4v b = {dk1[4 * q], dk1[4 * q + 1], dk1[4 * q + 2], dk1[4 * q + 3]};
+      *reinterpret_cast<float4v*>(kout + 8 * q) = a * s;
+      *reinterpret_cast<float4v*>(kout + 32 + 8 * q) = b * s;
+    }
+    float* vout = dVp + (size_t)h * kD * T + key;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int d = 8 * (i >> 2) + 4 * g + (i & 3);
+      vout[(size_t)d * T] = dv0[i];
+      vout[(size_t)(d + 32) * T] = dv1[i];
+    }
+  }
+}
+
+// -------------------------------------------------------------------------
+// Grouped gradient reduction: out[kv][e] = sum over z = 0..G-1, in order, of
+// planes[kv G + z][e], for the dK planes (blockIdx.z = 0) and the dV^T
+// planes (blockIdx.z = 1); a thread owns four consecutive elements.
+// -------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+sattn_bwd_reduce_kernel(const float* __restrict__ kPlanes, const float* __restrict__ vPlanes,
+                        float* __restrict__ dK, float* __restrict__ dVt, int planeQuads, int G) {
+  const int e4 = blockIdx.x * 256 + threadIdx.x;
+  if (e4 >= planeQuads) return;
+  const int kv = blockIdx.y;
+  const float* src = (blockIdx.z == 0 ? kPlanes : vPlanes) + (size_t)kv * G * planeQuads * 4;
+  float* dst = (blockIdx.z == 0 ? dK : dVt) + (size_t)kv * planeQuads * 4;
+  float4v acc = *reinterpret_cast<const float4v*>(src + (size_t)e4 * 4);
+  for (int z = 1; z < G; ++z)
+    acc += *reinterpret_cast<const float4v*>(src + ((size_t)z * planeQuads + e4) * 4);
+  *reinterpret_cast<float4v*>(dst + (size_t)e4 * 4) = acc;
+}
+
+// Per-device cache of "is gfx950": 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return SATTN_ERR_DEVICE;
+  if (dev < kMaxDevices) {
+    const int cached = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (cached != 0) return cached == 1 ? SATTN_OK : SATTN_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SATTN_ERR_DEVICE;
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? SATTN_OK : SATTN_ERR_DEVICE;
+}
+
+void launch_query(const half_t* Q, const half_t* K, const half_t* Vt, const half_t* O,
+                  const half_t* dO, const float* L, float* dQ, float* D, float c, float s, int T,
+                  int Hq, int Hkv, hipStream_t stream) {
+  const int nBlocks = (T + 32 * kNW - 1) / (32 * kNW);
+  const dim3 grid((unsigned)nBlocks * (unsigned)Hq);
+  if (T % 8 == 0)
+    hipLaunchKernelGGL(sattn_bwdq_kernel<true>, grid, dim3(64 * kNW), 0, stream, Q, K, Vt, O, dO,
+                       L, dQ, D, c, s, T, Hq, Hq / Hkv, nBlocks);
+  else
+    hipLaunchKernelGGL(sattn_bwdq_kernel<false>, grid, dim3(64 * kNW), 0, stream, Q, K, Vt, O, dO,
+                       L, dQ, D, c, s, T, Hq, Hq / Hkv, nBlocks);
+}
+
+void launch_key(const half_t* Q, const half_t* K, const half_t* Vt, const half_t* dO,
+                const float* L, const float* D, float* dK, float* dVt, void* ws, float c, float s,
+                int T, int Hq, int Hkv, hipStream_t stream) {
+  const int G = Hq / Hkv;
+  float* kp = G == 1 ? dK : static_cast<float*>(ws);
+  float* vp = G == 1 ? dVt : static_cast<float*>(ws) + (size_t)Hq * T * kD;
+  const int nBlocks = (T + 32 * kNW - 1) / (32 * kNW);
+  const dim3 grid((unsigned)nBlocks * (unsigned)Hq);
+  hipLaunchKernelGGL(sattn_bwdk_kernel<true>, grid, dim3(64 * kNW), 0, stream, Q, K, Vt, dO, L, D,
+                     kp, vp, c, s, T, Hq, G);
+  if (G > 1) {
+    const int planeQuads = T * kD / 4;
+    const dim3 rgrid((unsigned)((planeQuads + 255) / 256), (unsigned)Hkv, 2u);
+    hipLaunchKernelGGL(sattn_bwd_reduce_kernel, rgrid, dim3(256), 0, stream, kp, vp, dK, dVt,
+                       planeQuads, G);
+  }
+}
+
+}  // namespace
+
+extern "C" int sattn_bwd_query(const void* Q, const void* K, const void* Vt, const void* O,
+                               const void* dO, const float* L, float* dQ, float* D, float c,
+                               float s, int T, int Hq, int Hkv, void* stream) {
+  const int st = sattn_bwd_query_check(Q, K, Vt, O, dO, L, dQ, D, c, s, T, Hq, Hkv);
+  if (st != SATTN_OK) return st;
+  const int dst = check_device();
+  if (dst != SATTN_OK) return dst;
+  launch_query(static_cast<const half_t*>(Q), static_cast<const half_t*>(K),
+               static_cast<const half_t*>(Vt), static_cast<const half_t*>(O),
+               static_cast<const half_t*>(dO), L, dQ, D, c, s, T, Hq, Hkv,
+               static_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? SATTN_OK : SATTN_ERR_LAUNCH;
+}
+
+extern "C" int sattn_bwd_key(const void* Q, const void* K, const void* Vt, const void* dO,
+                             const float* L, const float* D, float* dK, float* dVt,
+                             void* workspace, unsigned long long workspace_bytes, float c,
+                             float s, int T, int Hq, int Hkv, void* stream) {
+  const int st = sattn_bwd_key_check(Q, K, Vt, dO, L, D, dK, dVt, workspace, workspace_bytes, c,
+                                     s, T, Hq, Hkv);
+  if (st != SATTN_OK) return st;
+  const int dst = check_device();
+  if (dst != SATTN_OK) return dst;
+  launch_key(static_cast<const half_t*>(Q), static_cast<const half_t*>(K),
+             static_cast<const half_t*>(Vt), static_cast<const half_t*>(dO), L, D, dK, dVt,
+             workspace, c, s, T, Hq, Hkv, static_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? SATTN_OK : SATTN_ERR_LAUNCH;
+}
+
+extern "C" int sattn_bwd(const void* Q, const void* K, const void* Vt, const void* O,
+                         const void* dO, const float* L, float* dQ, float* dK, float* dVt,
+                         float* D, void* workspace, unsigned long long workspace_bytes, float c,
+                         float s, int T, int Hq, int Hkv, void* stream) {
+  const int st = sattn_bwd_check(Q, K, Vt, O, dO, L, dQ, dK, dVt, D, workspace, workspace_bytes,
+                                 c, s, T, Hq, Hkv);
+  if (st != SATTN_OK) return st;
+  const int dst = check_device();
+  if (dst != SATTN_OK) return dst;
+  const hipStream_t strm = static_cast<hipStream_t>(stream);
+  const half_t* q = static_cast<const half_t*>(Q);
+  const half_t* k = static_cast<const half_t*>(K);
+  const half_t* v = static_cast<const half_t*>(Vt);
+  const half_t* g = static_cast<const half_t*>(dO);
+  launch_query(q, k, v, static_cast<const half_t*>(O), g, L, dQ, D, c, s, T, Hq, Hkv, strm);
+  launch_key(q, k, v, g, L, D, dK, dVt, workspace, c, s, T, Hq, Hkv, strm);
+  return hipGetLastError() == hipSuccess ? SATTN_OK : SATTN_ERR_LAUNCH;
+}

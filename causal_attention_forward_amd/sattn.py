@@ -50,6 +50,21 @@ _lib.sattn_fwd_check.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void
                                  ctypes.c_int, ctypes.c_int, ctypes.c_int]
 _lib.sattn_status_string.restype = ctypes.c_char_p
 _lib.sattn_status_string.argtypes = [ctypes.c_int]
+_P, _F, _I, _U64 = ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_ulonglong
+_lib.sattn_bwd_query.restype = ctypes.c_int
+_lib.sattn_bwd_query.argtypes = [_P] * 8 + [_F, _F, _I, _I, _I, _P]
+_lib.sattn_bwd_key.restype = ctypes.c_int
+_lib.sattn_bwd_key.argtypes = [_P] * 9 + [_U64, _F, _F, _I, _I, _I, _P]
+_lib.sattn_bwd.restype = ctypes.c_int
+_lib.sattn_bwd.argtypes = [_P] * 11 + [_U64, _F, _F, _I, _I, _I, _P]
+_lib.sattn_bwd_workspace_bytes.restype = ctypes.c_ulonglong
+_lib.sattn_bwd_workspace_bytes.argtypes = [_I, _I, _I]
+_lib.sattn_bwd_check.restype = ctypes.c_int
+_lib.sattn_bwd_check.argtypes = [_P] * 11 + [_U64, _F, _F, _I, _I, _I]
+_lib.sattn_bwd_query_check.restype = ctypes.c_int
+_lib.sattn_bwd_query_check.argtypes = [_P] * 8 + [_F, _F, _I, _I, _I]
+_lib.sattn_bwd_key_check.restype = ctypes.c_int
+_lib.sattn_bwd_key_check.argtypes = [_P] * 9 + [_U64, _F, _F, _I, _I, _I]
 
 SATTN_OK = 0
 SATTN_ERR_NULL = 1
@@ -59,9 +74,12 @@ SATTN_ERR_ALIGN = 4
 SATTN_ERR_ALIAS = 5
 SATTN_ERR_DEVICE = 6
 SATTN_ERR_LAUNCH = 7
+SATTN_ERR_WORKSPACE = 8
 HEAD_DIM = 64
 
-EXPORTS = ("sattn_fwd", "sattn_fwd_check", "sattn_status_string")
+EXPORTS = ("sattn_fwd", "sattn_fwd_check", "sattn_status_string", "sattn_bwd_query",
+           "sattn_bwd_key", "sattn_bwd", "sattn_bwd_workspace_bytes", "sattn_bwd_check",
+           "sattn_bwd_query_check", "sattn_bwd_key_check")
 
 
 class SattnError(RuntimeError):
@@ -118,3 +136,104 @@ def fwd(q, k, vt, c, out=None, lse=None, stream=None):
     if st != SATTN_OK:
         raise SattnError(st)
     return out, lse
+
+
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+def sattn_bwd_workspace_bytes(T: int, Hq: int, Hkv: int) -> int:
+    return int(_lib.sattn_bwd_workspace_bytes(T, Hq, Hkv))
+
+
+def sattn_bwd_check(Q, K, Vt, O, dO, L, dQ, dK, dVt, D, ws, ws_bytes, c, s, T, Hq, Hkv) -> int:
+    """Host-side validation only (no HIP call); returns the status code."""
+    return _lib.sattn_bwd_check(Q, K, Vt, O, dO, L, dQ, dK, dVt, D, ws, ws_bytes,
+                                ctypes.c_float(c), ctypes.c_float(s), T, Hq, Hkv)
+
+
+def sattn_bwd_query_check(Q, K, Vt, O, dO, L, dQ, D, c, s, T, Hq, Hkv) -> int:
+    return _lib.sattn_bwd_query_check(Q, K, Vt, O, dO, L, dQ, D, ctypes.c_float(c),
+                                      ctypes.c_float(s), T, Hq, Hkv)
+
+
+def sattn_bwd_key_check(Q, K, Vt, dO, L, D, dK, dVt, ws, ws_bytes, c, s, T, Hq, Hkv) -> int:
+    return _lib.sattn_bwd_key_check(Q, K, Vt, dO, L, D, dK, dVt, ws, ws_bytes, ctypes.c_float(c),
+                                    ctypes.c_float(s), T, Hq, Hkv)
+
+
+def sattn_bwd(Q, K, Vt, O, dO, L, dQ, dK, dVt, D, ws, ws_bytes, c, s, T, Hq, Hkv,
+              stream=None) -> int:
+    """The C entry point with raw device addresses; returns the status code."""
+    return _lib.sattn_bwd(Q, K, Vt, O, dO, L, dQ, dK, dVt, D, ws, ws_bytes, ctypes.c_float(c),
+                          ctypes.c_float(s), T, Hq, Hkv, stream)
+
+
+def sattn_bwd_query(Q, K, Vt, O, dO, L, dQ, D, c, s, T, Hq, Hkv, stream=None) -> int:
+    return _lib.sattn_bwd_query(Q, K, Vt, O, dO, L, dQ, D, ctypes.c_float(c), ctypes.c_float(s),
+                                T, Hq, Hkv, stream)
+
+
+def sattn_bwd_key(Q, K, Vt, dO, L, D, dK, dVt, ws, ws_bytes, c, s, T, Hq, Hkv,
+                  stream=None) -> int:
+    return _lib.sattn_bwd_key(Q, K, Vt, dO, L, D, dK, dVt, ws, ws_bytes, ctypes.c_float(c),
+                              ctypes.c_float(s), T, Hq, Hkv, stream)
+
+
+def _check_half(name, x, shape):
+    import torch
+    if tuple(x.shape) != tuple(shape) or x.dtype != torch.float16 or not x.is_cuda \
+            or not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float16 GPU tensor of shape {tuple(shape)}")
+
+
+def _out(x, shape, dev):
+    import torch
+    if x is None:
+        return torch.empty(shape, dtype=torch.float32, device=dev)
+    if tuple(x.shape) != tuple(shape) or x.dtype != torch.float32 or not x.is_contiguous():
+        raise ValueError(f"outputs must be contiguous float32 of shape {tuple(shape)}")
+    return x
+
+
+def bwd(q, k, vt, o, do, lse, c, s, dq=None, dk=None, dvt=None, D=None, workspace=None,
+        stream=None):
+    """Attention backward on torch GPU tensors (query launch, then key launch
+    and the grouped reduction).
+
+    q [Hq][T][64], k [Hkv][T][64], vt [Hkv][64][T], o and do [T][Hq*64]
+    (float16, contiguous), lse float32 [Hq][T] (the forward's L); c the
+    base-2 and s the natural score scale.  Returns ``(dQ, dK, dVt, D)``:
+    float32 [Hq][T][64], [Hkv][T][64], [Hkv][64][T] and [Hq][T].  The
+    workspace (uint8, at least ``sattn_bwd_workspace_bytes`` bytes) is
+    allocated here unless given.
+    """
+    import torch
+    Hq, T, _ = q.shape
+    Hkv = k.shape[0]
+    _check_half("q", q, (Hq, T, HEAD_DIM))
+    _check_half("k", k, (Hkv, T, HEAD_DIM))
+    _check_half("vt", vt, (Hkv, HEAD_DIM, T))
+    _check_half("o", o, (T, Hq * HEAD_DIM))
+    _check_half("do", do, (T, Hq * HEAD_DIM))
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, T) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [Hq][T]")
+    dev = q.device
+    dq = _out(dq, (Hq, T, HEAD_DIM), dev)
+    dk = _out(dk, (Hkv, T, HEAD_DIM), dev)
+    dvt = _out(dvt, (Hkv, HEAD_DIM, T), dev)
+    D = _out(D, (Hq, T), dev)
+    need = sattn_bwd_workspace_bytes(T, Hq, Hkv)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = sattn_bwd(q.data_ptr(), k.data_ptr(), vt.data_ptr(), o.data_ptr(), do.data_ptr(),
+                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dvt.data_ptr(),
+                       D.data_ptr(), ws_ptr, ws_bytes, float(c), float(s), T, Hq, Hkv,
+                       stream.cuda_stream)
+    if st != SATTN_OK:
+        raise SattnError(st)
+    return dq, dk, dvt, D

@@ -1,5 +1,6 @@
 /*
- * libsattn: the causal streaming-attention forward on AMD MI355X (gfx950).
+ * libsattn: causal streaming attention, forward and backward, on AMD MI355X
+ * (gfx950).
  *
  * What is computed (StreamingAttentionSM86 page, header comment of the forward
  * realization): for every query head h and query row i,
@@ -31,14 +32,15 @@ extern "C" {
 
 typedef enum {
   SATTN_OK = 0,
-  SATTN_ERR_NULL = 1,   /* Q, K, Vt, O or L is NULL                                  */
+  SATTN_ERR_NULL = 1,   /* a required pointer is NULL                               */
   SATTN_ERR_SHAPE = 2,  /* T < 1, Hq < 1, Hkv < 1, Hq % Hkv != 0, Hq > 65535, or
                            Hq * 64 * T * 4 > 2^32 - 1                                 */
-  SATTN_ERR_SCALE = 3,  /* c is not finite or c <= 0                                  */
-  SATTN_ERR_ALIGN = 4,  /* Q, K, Vt or O not 16-byte aligned, or L not 4-byte aligned */
-  SATTN_ERR_ALIAS = 5,  /* O or L overlaps Q, K, Vt, or each other                    */
+  SATTN_ERR_SCALE = 3,  /* c (or the backward's s) is not finite, or is <= 0         */
+  SATTN_ERR_ALIGN = 4,  /* a pointer is less aligned than its entry point requires    */
+  SATTN_ERR_ALIAS = 5,  /* an output overlaps an input or another output              */
   SATTN_ERR_DEVICE = 6, /* no current HIP device, or it is not gfx950                 */
-  SATTN_ERR_LAUNCH = 7  /* the kernel launch was refused (hipGetLastError)            */
+  SATTN_ERR_LAUNCH = 7, /* the kernel launch was refused (hipGetLastError)            */
+  SATTN_ERR_WORKSPACE = 8 /* the backward's workspace is NULL or smaller than needed   */
 } sattn_status;
 
 /*
@@ -82,6 +84,106 @@ int sattn_fwd(const void* Q, const void* K, const void* Vt, void* O, float* L,
  */
 int sattn_fwd_check(const void* Q, const void* K, const void* Vt, const void* O,
                     const float* L, float c, int T, int Hq, int Hkv);
+
+/*
+ * The backward (StreamingAttentionSM86 page: the comment that opens the
+ * backward pass and those of its query launch, key launch and grouped
+ * gradient reduction).  With the forward's O and L and the output gradient
+ * dO, and P_ij = 2^(c (q_i . k_j) - L_i) for keys j <= i (else 0):
+ *
+ *     D_i   = sum_d dO_id O_id            (the row term)
+ *     dP_ij = dO_i . v_j,   dS_ij = P_ij (dP_ij - D_i)
+ *     dQ_i  = s sum_j dS_ij k_j
+ *     dK_j  = s sum_i dS_ij q_i,   dV_j = sum_i P_ij dO_i
+ *
+ * where the key gradients of a K/V head are summed over the G query heads of
+ * its group.  P and dS are rounded to binary16 (round to nearest even) as the
+ * operands of the products that follow; every sum is binary32.  With
+ * c = s log2(e) and the forward's own O and L these are the gradients of
+ * sum(dO * O) with respect to Q, K and V.  Deterministic: no atomics, and
+ * the group sum is taken in a fixed order, so the same inputs give the same
+ * bits on every run.
+ *
+ * Shared arguments (layouts as in sattn_fwd):
+ *   Q    device, binary16 [Hq][T][64];  K  device, binary16 [Hkv][T][64]
+ *   Vt   device, binary16 [Hkv][64][T]
+ *   O    device, binary16 [T][Hq*64], the forward's output (token-major)
+ *   dO   device, binary16 [T][Hq*64], the output gradient, laid out like O
+ *   L    device, binary32 [Hq][T], the forward's base-2 log-sum-exp
+ *   c    binary32 base-2 score scale (finite, > 0), as given to sattn_fwd
+ *   s    binary32 natural score scale (finite, > 0) applied to dQ and dK
+ *   T, Hq, Hkv as in sattn_fwd; stream a hipStream_t or NULL
+ * Buffers are the caller's and nothing is retained; inputs may overlap one
+ * another, outputs may overlap nothing.  Pointers to binary16 data must be
+ * 16-byte aligned, to binary32 data 16-byte aligned (L: 4-byte).  Arguments
+ * are validated before anything is enqueued (on error nothing is launched and
+ * no output is touched); calls are asynchronous like sattn_fwd.
+ */
+
+/*
+ * sattn_bwd_query: the query launch.  Writes the row term D (binary32
+ * [Hq][T], every element) and dQ (binary32 [Hq][T][64], row-major per query
+ * head, every element).
+ */
+int sattn_bwd_query(const void* Q, const void* K, const void* Vt, const void* O,
+                    const void* dO, const float* L, float* dQ, float* D, float c, float s,
+                    int T, int Hq, int Hkv, void* stream);
+
+/*
+ * sattn_bwd_key: the key launch and, when Hq > Hkv, the grouped gradient
+ * reduction.  Reads D as written by sattn_bwd_query (enqueue that first on the
+ * same stream).  Writes dK (binary32 [Hkv][T][64]) and the V gradient
+ * transposed like V^T, dVt (binary32 [Hkv][64][T]); every element of both.
+ *
+ *   workspace        device scratch of at least sattn_bwd_workspace_bytes()
+ *                    bytes, 16-byte aligned, holding one dK and one dV^T
+ *                    plane per query head between the two launches; may be
+ *                    NULL when that size is 0.  Its contents on entry do not
+ *                    matter; on return they are unspecified.  Calls that share
+ *                    a workspace must be ordered (one stream).
+ *   workspace_bytes  its size; SATTN_ERR_WORKSPACE if too small.
+ */
+int sattn_bwd_key(const void* Q, const void* K, const void* Vt, const void* dO,
+                  const float* L, const float* D, float* dK, float* dVt, void* workspace,
+                  unsigned long long workspace_bytes, float c, float s, int T, int Hq, int Hkv,
+                  void* stream);
+
+/*
+ * sattn_bwd: sattn_bwd_query then sattn_bwd_key on `stream`; the outputs of
+ * both (D is an output too).
+ */
+int sattn_bwd(const void* Q, const void* K, const void* Vt, const void* O, const void* dO,
+              const float* L, float* dQ, float* dK, float* dVt, float* D, void* workspace,
+              unsigned long long workspace_bytes, float c, float s, int T, int Hq, int Hkv,
+              void* stream);
+
+/* sattn_bwd_workspace_bytes: the workspace sattn_bwd_key and sattn_bwd need:
+ * 0 when Hq == Hkv, else 2 * Hq * T * 64 * 4 bytes; 0 for shapes that
+ * sattn_bwd_check rejects.  Makes no HIP call. */
+unsigned long long sattn_bwd_workspace_bytes(int T, int Hq, int Hkv);
+
+/*
+ * sattn_bwd_check: the host-side validation of sattn_bwd alone (shape rule
+ * and scales as for sattn_fwd, s finite and > 0, alignment, outputs
+ * overlapping nothing, workspace size).  Makes no HIP call and dereferences
+ * nothing.  sattn_bwd_query and sattn_bwd_key apply the parts that concern
+ * their own arguments.
+ */
+int sattn_bwd_check(const void* Q, const void* K, const void* Vt, const void* O, const void* dO,
+                    const float* L, const float* dQ, const float* dK, const float* dVt,
+                    const float* D, const void* workspace, unsigned long long workspace_bytes,
+                    float c, float s, int T, int Hq, int Hkv);
+
+/* sattn_bwd_query_check, sattn_bwd_key_check: the validation that
+ * sattn_bwd_query and sattn_bwd_key apply to their own arguments (the parts
+ * of sattn_bwd_check that concern them).  No HIP call, no dereference. */
+int sattn_bwd_query_check(const void* Q, const void* K, const void* Vt, const void* O,
+                          const void* dO, const float* L, const float* dQ, const float* D,
+                          float c, float s, int T, int Hq, int Hkv);
+int sattn_bwd_key_check(const void* Q, const void* K, const void* Vt, const void* dO,
+                        const float* L, const float* D, const float* dK, const float* dVt,
+                        const void* workspace, unsigned long long workspace_bytes, float c,
+                        float s, int T, int Hq, int Hkv);
 
 /* sattn_status_string: a static, NUL-terminated description of a status code
  * (an unknown code gives "unknown sattn status").  Never NULL. */

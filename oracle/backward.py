@@ -141,16 +141,16 @@ def backward_key_rows_ref(Q, K, Vt, O, dO, L, c, s, kv: int, keys):
     c, s = float(c), float(s)
     G = Hq // Hkv
     keys = list(keys)
-    D = row_terms_ref(O, dO, Hq)
     out = {"dK": np.zeros((len(keys), HEAD_DIM)), "dV": np.zeros((len(keys), HEAD_DIM)),
            "P": np.zeros((G, T, len(keys))), "dS": np.zeros((G, T, len(keys)))}
     for z in range(G):
         h = kv * G + z
-        _, q, k, v, do, _, l = _head(h, Q, K, Vt, O, dO, L, Hq, Hkv)
+        _, q, k, v, do, o, l = _head(h, Q, K, Vt, O, dO, L, Hq, Hkv)
+        Dh = (do * o).sum(axis=1)                 # the row terms of head h
         for n, j in enumerate(keys):
             t = (q[j:] @ k[j]) * c                # queries i >= j see key j
             P = np.exp2(t - l[j:])
-            dS = P * (do[j:] @ v[j] - D[h, j:])
+            dS = P * (do[j:] @ v[j] - Dh[j:])
             out["dK"][n] += s * (dS @ q[j:])
             out["dV"][n] += P @ do[j:]
             out["P"][z, j:, n] = P
