@@ -61,7 +61,7 @@ typedef int int4v __attribute__((ext_vector_type(4)));
 
 constexpr int kD = SATTN_HEAD_DIM;              // head width
 constexpr int kTile = 64;                       // rows of a staged K, V^T, Q or dO tile
-constexpr int kRowHalfs = kD + 8;               // LDS row: 64 values + 16 bytes of padding
+constexpr int kRowHalfs = kD;                   // LDS row: 64 values, 16-byte chunks swizzled
 constexpr int kTileHalfs = kTile * kRowHalfs;
 constexpr int kBufferWord3 = 0x00020000;        // raw buffer, 32-bit data format
 constexpr int kOutOfRange = 0x7FFFFFF0;         // a buffer offset past every range
@@ -95,21 +95,41 @@ __device__ __forceinline__ half4 lds_tr4(const half_t* p) {
   return __builtin_bit_cast(half4, v);
 }
 
-// Operand whose lane l holds X[m][k0 + 8(l/32) .. +7] for a tile stored
-// k-major in LDS (X[m][k] at row k, column m): two transpose reads, rows
-// k .. k+3 and k+4 .. k+7.  `p` already includes the lane's own offset.
-__device__ __forceinline__ half8 tr8(const half_t* p) {
-  const half4 lo = lds_tr4(p), hi = lds_tr4(p + 4 * kRowHalfs);
-  return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+// LDS tiles keep 64-value rows unpadded and place 16-byte chunk c of row r at
+// chunk c ^ swz(r), swz(r) = the three bits of (r/2) % 8 reversed.  Sixteen
+// lanes reading one chunk of 16 consecutive rows (the natural operand read)
+// then hit all 64 banks once, and so do 32 lanes of a transpose read (four
+// rows, four chunks each): rows r and r+2 land in opposite halves of the row
+// and odd rows in the other 32 banks.  The pad of the forward's tiles cannot do
+// both.  swz depends on r only through (r/2) % 8, so an offset of 16 rows
+// keeps it.
+__device__ __forceinline__ int swz(int r) {
+  const int v = (r >> 1) & 7;
+  return ((v & 1) << 2) | (v & 2) | (v >> 2);
 }
 
-// A lane's offset (halfs) for tr8 over a k-major tile: row 8(l/32) + (l%16)/4,
-// column 16((l/16)%2) + 4 c(l%4), where c is the identity (the operand's row m
-// is l%32) or swaps the two bits of l%4 (its row m is krow(l%32)).
-__device__ __forceinline__ int tr_offset(int lane, bool permuted) {
+// Offset (halfs) of 16-byte chunk c of row r in a swizzled tile.
+__device__ __forceinline__ int chunk_offset(int r, int c) { return r * kRowHalfs + ((c ^ swz(r)) << 3); }
+
+// Operand whose lane l holds X[m][k0 + 8(l/32) .. +7] for a tile stored
+// k-major in LDS (X[m][k] at row k, column m): two transpose reads, rows
+// k .. k+3 at lo and k+4 .. k+7 at hi (offsets include the lane's own part).
+__device__ __forceinline__ half8 tr8(const half_t* base, int lo, int hi) {
+  const half4 a = lds_tr4(base + lo), b = lds_tr4(base + hi);
+  return half8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// A lane's tr8 offset (halfs) over a k-major tile for operand rows m in
+// 32 mh .. 32 mh + 31 and the read of rows 4 hi .. (hi = 0, 1): row
+// 8(l/32) + (l%16)/4 + 4 hi, column 32 mh + 16((l/16)%2) + 4 c(l%4), where c
+// is the identity (the operand's row m is l%32) or swaps the two bits of l%4
+// (its row m is krow(l%32)).
+__device__ __forceinline__ int tr_offset(int lane, bool permuted, int mh, int hi) {
   const int b = lane & 3;
   const int cb = permuted ? (((b & 1) << 1) | (b >> 1)) : b;
-  return (8 * (lane >> 5) + ((lane & 15) >> 2)) * kRowHalfs + 16 * ((lane >> 4) & 1) + 4 * cb;
+  const int row = 8 * (lane >> 5) + ((lane & 15) >> 2) + 4 * hi;
+  const int col = 32 * mh + 16 * ((lane >> 4) & 1) + 4 * cb;
+  return chunk_offset(row, col >> 3) + (col & 7);
 }
 
 // binary16 operand of 16 consecutive indices from accumulator elements
@@ -203,15 +223,25 @@ sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
   auto store = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const int off = buf * kTileHalfs + (cr + 32 * p) * kRowHalfs + cc * 8;
+      const int off = buf * kTileHalfs + chunk_offset(cr + 32 * p, cc);
       *reinterpret_cast<int4v*>(kbuf + off) = kst[p];
       *reinterpret_cast<int4v*>(vbuf + off) = vst[p];
     }
   };
 
-  const int kOff = krow(n) * kRowHalfs + 8 * g;  // natural K rows for S^T (keys krow(n))
-  const int vtOff = tr_offset(lane, true);      // V rows (keys krow(n)) from the V^T tile
-  const int ktOff = tr_offset(lane, false);     // K^T rows (d = n) from the K tile
+  // natural K rows for S^T (keys krow(n), d = 16kk + 8g ..)
+  int kOff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) kOff[kk] = chunk_offset(krow(n), 2 * kk + g);
+  // V rows (keys krow(n) + 32 mh) from the V^T tile; K^T rows (d = n + 32 mh) from the K tile
+  int vtOff[2][2], ktOff[2][2];
+#pragma unroll
+  for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      vtOff[mh][hi] = tr_offset(lane, true, mh, hi);
+      ktOff[mh][hi] = tr_offset(lane, false, mh, hi);
+    }
 
   float16v dq0 = {}, dq1 = {};
   load(0);
@@ -227,12 +257,13 @@ sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
       float16v s0, s1, p0, p1;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const half8 a0 = ld8(kb + kOff + 16 * kk);
-        const half8 a1 = ld8(kb + kOff + 32 * kRowHalfs + 16 * kk);
+        const half8 a0 = ld8(kb + kOff[kk]);
+        const half8 a1 = ld8(kb + kOff[kk] + 32 * kRowHalfs);
         s0 = mfma(a0, qf[kk], kk == 0 ? float16v{} : s0);
         s1 = mfma(a1, qf[kk], kk == 0 ? float16v{} : s1);
-        const half8 v0 = tr8(vb + vtOff + 16 * kk * kRowHalfs);
-        const half8 v1 = tr8(vb + vtOff + 16 * kk * kRowHalfs + 32);
+        const half_t* vk = vb + 16 * kk * kRowHalfs;
+        const half8 v0 = tr8(vk, vtOff[0][0], vtOff[0][1]);
+        const half8 v1 = tr8(vk, vtOff[1][0], vtOff[1][1]);
         p0 = mfma(v0, dof[kk], kk == 0 ? float16v{} : p0);
         p1 = mfma(v1, dof[kk], kk == 0 ? float16v{} : p1);
       }
@@ -256,8 +287,9 @@ sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
       // dQ^T += K^T dS^T: d = n (dq0) and 32 + n (dq1), keys 16ck + 8g .. +7
 #pragma unroll
       for (int ck = 0; ck < 4; ++ck) {
-        const half8 k0 = tr8(kb + ktOff + 16 * ck * kRowHalfs);
-        const half8 k1 = tr8(kb + ktOff + 16 * ck * kRowHalfs + 32);
+        const half_t* kc = kb + 16 * ck * kRowHalfs;
+        const half8 k0 = tr8(kc, ktOff[0][0], ktOff[0][1]);
+        const half8 k1 = tr8(kc, ktOff[1][0], ktOff[1][1]);
         dq0 = mfma(k0, ds[ck], dq0);
         dq1 = mfma(k1, ds[ck], dq1);
       }
@@ -353,15 +385,23 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
   auto store = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const int off = buf * kTileHalfs + (cr + 32 * p) * kRowHalfs + cc * 8;
+      const int off = buf * kTileHalfs + chunk_offset(cr + 32 * p, cc);
       *reinterpret_cast<int4v*>(qbuf + off) = qst[p];
       *reinterpret_cast<int4v*>(obuf + off) = ost[p];
     }
     if (tid < 2 * kTile) rowterms[buf][tid >> 6][tid & (kTile - 1)] = rst;
   };
 
-  const int nOff = krow(n) * kRowHalfs + 8 * g;  // natural Q / dO rows (queries krow(n))
-  const int tOff = tr_offset(lane, false);       // Q^T / dO^T rows (d = n)
+  // natural Q / dO rows (queries krow(n), d = 16kk + 8g ..)
+  int nOff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) nOff[kk] = chunk_offset(krow(n), 2 * kk + g);
+  // Q^T / dO^T rows (d = n + 32 mh)
+  int tOff[2][2];
+#pragma unroll
+  for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) tOff[mh][hi] = tr_offset(lane, false, mh, hi);
 
   float16v dk0 = {}, dk1 = {}, dv0 = {}, dv1 = {};
   load(ft);
@@ -377,12 +417,12 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
       float16v s0, s1, p0, p1;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const half8 a0 = ld8(qb + nOff + 16 * kk);
-        const half8 a1 = ld8(qb + nOff + 32 * kRowHalfs + 16 * kk);
+        const half8 a0 = ld8(qb + nOff[kk]);
+        const half8 a1 = ld8(qb + nOff[kk] + 32 * kRowHalfs);
         s0 = mfma(a0, kf[kk], kk == 0 ? float16v{} : s0);
         s1 = mfma(a1, kf[kk], kk == 0 ? float16v{} : s1);
-        const half8 b0 = ld8(ob + nOff + 16 * kk);
-        const half8 b1 = ld8(ob + nOff + 32 * kRowHalfs + 16 * kk);
+        const half8 b0 = ld8(ob + nOff[kk]);
+        const half8 b1 = ld8(ob + nOff[kk] + 32 * kRowHalfs);
         p0 = mfma(b0, vf[kk], kk == 0 ? float16v{} : p0);
         p1 = mfma(b1, vf[kk], kk == 0 ? float16v{} : p1);
       }
@@ -424,12 +464,14 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
       // queries 16ck + 8g .. +7
 #pragma unroll
       for (int ck = 0; ck < 4; ++ck) {
-        const half8 o0 = tr8(ob + tOff + 16 * ck * kRowHalfs);
-        const half8 o1 = tr8(ob + tOff + 16 * ck * kRowHalfs + 32);
+        const half_t* oc = ob + 16 * ck * kRowHalfs;
+        const half_t* qc = qb + 16 * ck * kRowHalfs;
+        const half8 o0 = tr8(oc, tOff[0][0], tOff[0][1]);
+        const half8 o1 = tr8(oc, tOff[1][0], tOff[1][1]);
         dv0 = mfma(o0, pb[ck], dv0);
         dv1 = mfma(o1, pb[ck], dv1);
-        const half8 q0 = tr8(qb + tOff + 16 * ck * kRowHalfs);
-        const half8 q1 = tr8(qb + tOff + 16 * ck * kRowHalfs + 32);
+        const half8 q0 = tr8(qc, tOff[0][0], tOff[0][1]);
+        const half8 q1 = tr8(qc, tOff[1][0], tOff[1][1]);
         dk0 = mfma(q0, db[ck], dk0);
         dk1 = mfma(q1, db[ck], dk1);
       }
