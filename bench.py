@@ -270,6 +270,8 @@ def main():
                          "(median of 5 timed runs, input sets rotated so small ones are not cache figures)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (sattn_bwd) instead of the forward")
+    ap.add_argument("--vrows", action="store_true",
+                    help="time the forward taking V as rows (sattn_fwd_vrows) instead of V^T")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the attention, run device-to-device copies of MIB MiB "
                          "(the reference transfer for scaling HBM byte counters)")
@@ -311,9 +313,36 @@ def main():
     O = torch.empty((x.T, x.Hq * 64), dtype=torch.float16, device=dev)
     L = torch.empty((x.Hq, x.T), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    extra = {}
+    if args.vrows:
+        v = vt.transpose(1, 2).contiguous()   # V as rows [Hkv][T][64]
 
-    def step():
-        sattn.fwd(q, k, vt, x.c, out=O, lse=L, stream=stream)
+        def step():
+            sattn.fwd_vrows(q, k, v, x.c, out=O, lse=L, stream=stream)
+
+        # what V rows replace: the V^T kernel on the same values, plus the
+        # V -> V^T transpose it needs first (torch's copy kernel, for scale)
+        def vt_step():
+            sattn.fwd(q, k, vt, x.c, out=O, lse=L, stream=stream)
+
+        def transpose():
+            vt.copy_(v.transpose(1, 2))
+
+        def extras():  # after the timed region, on a warm GPU
+            for fn, key in ((vt_step, "vt_path_kernel_ms"), (transpose, "v_transpose_ms")):
+                for _ in range(50):
+                    fn()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(200):
+                    fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                extra[key] = round(e0.elapsed_time(e1) / 200, 5)
+    else:
+        extras = None
+        def step():
+            sattn.fwd(q, k, vt, x.c, out=O, lse=L, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -328,14 +357,17 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kernel_ms = ev0.elapsed_time(ev1) / args.steps  # average launch duration on the stream
+    if extras is not None:
+        extras()
 
     flops = causal_flops(x.T, x.Hq)
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
-    traffic = measured_traffic()
+    traffic = None if args.vrows else measured_traffic()
     out = {
-        "metric": "causal attn fwd TFLOP/s and % fp16 MFMA peak, T=4096 Hq=32 Hkv=8 d=64",
+        "metric": ("causal attn fwd (V as rows) TFLOP/s, T=4096 Hq=32 Hkv=8 d=64" if args.vrows else
+                   "causal attn fwd TFLOP/s and % fp16 MFMA peak, T=4096 Hq=32 Hkv=8 d=64"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -347,8 +379,9 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic",
-        "config": {"workload": w.name, "T": x.T, "Hq": x.Hq, "Hkv": x.Hkv, "head_dim": 64,
-                   "causal": True, "flop_per_call": flops, "pct_fp16_peak": round(100 * value / PEAK_FP16_TFLOPS, 2)},
+        "config": {"workload": w.name + (" V rows" if args.vrows else ""), "T": x.T, "Hq": x.Hq,
+                   "Hkv": x.Hkv, "head_dim": 64, "causal": True, "flop_per_call": flops,
+                   "pct_fp16_peak": round(100 * value / PEAK_FP16_TFLOPS, 2), **extra},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
                      "traffic": traffic, "kernel_ms": round(kernel_ms, 5)},

@@ -34,8 +34,9 @@
 //    of anything is written to memory.
 //  * A wave owns 32 queries (query launch) or 32 keys (key launch); a
 //    workgroup is four waves on consecutive rows and stages each 64-row tile
-//    once for all of them, double-buffered.  Workgroups are issued heaviest
-//    first.
+//    once for all of them, double-buffered.  Each XCD receives a contiguous
+//    run of workgroups ordered K/V head first (that head's tiles stay in its
+//    L2), then heaviest first.
 //  * With GQA the key launch writes one dK and one dV^T plane per query head
 //    into a caller-provided workspace and a reduction sums the G planes of
 //    each K/V head in head order; with Hq == Hkv it writes dK and dV^T
@@ -66,6 +67,16 @@ constexpr int kTileHalfs = kTile * kRowHalfs;
 constexpr int kBufferWord3 = 0x00020000;        // raw buffer, 32-bit data format
 constexpr int kOutOfRange = 0x7FFFFFF0;         // a buffer offset past every range
 constexpr int kNW = 4;                          // waves per workgroup
+constexpr int kXcds = 8;                        // accelerator complex dies per MI355X
+
+// Workgroups are dealt to the eight XCDs round-robin by index.  This returns
+// the workgroup's place in an order where each XCD receives one contiguous
+// run, so a run that covers one K/V head keeps that head's tiles in one L2.
+__device__ __forceinline__ int xcd_order() {
+  const int n = gridDim.x, b = blockIdx.x;
+  const int xcd = b % kXcds, idx = b / kXcds;
+  return xcd * (n / kXcds) + min(xcd, n % kXcds) + idx;
+}
 
 __device__ __forceinline__ float16v mfma(half8 a, half8 b, float16v c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -161,9 +172,12 @@ sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
   const int n = lane & 31;
   const int g = lane >> 5;
 
-  const int blk = nBlocks - 1 - (int)blockIdx.x / Hq;  // heaviest first
-  const int h = (int)blockIdx.x % Hq;
-  const int kv = h / G;
+  // K/V head first, then query blocks heaviest first, then the group's heads
+  const int lid = xcd_order();
+  const int kv = lid / (nBlocks * G);
+  const int rem = lid - kv * nBlocks * G;
+  const int blk = nBlocks - 1 - rem / G;
+  const int h = kv * G + rem % G;
   const int row0 = blk * 32 * kNW;
   const int waveRow0 = row0 + 32 * wave;
   const int row = waveRow0 + n;
@@ -321,7 +335,7 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
                   const half_t* __restrict__ Vt, const half_t* __restrict__ dO,
                   const float* __restrict__ L, const float* __restrict__ D,
                   float* __restrict__ dKp, float* __restrict__ dVp, float c, float s, int T,
-                  int Hq, int G) {
+                  int Hq, int G, int nBlocks) {
   __shared__ __attribute__((aligned(16))) half_t smem[4 * kTileHalfs];
   __shared__ __attribute__((aligned(16))) float rowterms[2][2][kTile];  // [buf][L, D][query]
   half_t* const qbuf = smem;                    // Q tiles [2][64 queries][72]
@@ -333,9 +347,12 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
   const int n = lane & 31;
   const int g = lane >> 5;
 
-  const int blk = (int)blockIdx.x / Hq;  // key block 0 has the most queries: heaviest first
-  const int h = (int)blockIdx.x % Hq;
-  const int kv = h / G;
+  // K/V head first, then key blocks heaviest (first) first, then the group's heads
+  const int lid = xcd_order();
+  const int kv = lid / (nBlocks * G);
+  const int rem = lid - kv * nBlocks * G;
+  const int blk = rem / G;
+  const int h = kv * G + rem % G;
   const int key0 = blk * 32 * kNW;
   const int waveKey0 = key0 + 32 * wave;
   const int key = waveKey0 + n;
@@ -559,7 +576,7 @@ void launch_key(const half_t* Q, const half_t* K, const half_t* Vt, const half_t
   const int nBlocks = (T + 32 * kNW - 1) / (32 * kNW);
   const dim3 grid((unsigned)nBlocks * (unsigned)Hq);
   hipLaunchKernelGGL(sattn_bwdk_kernel<true>, grid, dim3(64 * kNW), 0, stream, Q, K, Vt, dO, L, D,
-                     kp, vp, c, s, T, Hq, G);
+                     kp, vp, c, s, T, Hq, G, nBlocks);
   if (G > 1) {
     const int planeQuads = T * kD / 4;
     const dim3 rgrid((unsigned)((planeQuads + 255) / 256), (unsigned)Hkv, 2u);

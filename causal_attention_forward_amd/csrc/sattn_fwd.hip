@@ -130,7 +130,33 @@ __device__ __forceinline__ int krow(int m) {
   return 16 * (a >> 1) + 8 * e + 4 * (a & 1) + b;
 }
 
-template <int NW, int GW, bool VT_VEC>
+// V given as rows ([head][T][64]) is staged like K, in unpadded 64-value rows
+// whose 16-byte chunk c of row r sits at chunk c ^ vswz(r) (vswz(r) = the bits
+// of (r/2) % 8 reversed), and its V^T operand is read with the LDS transpose
+// read ds_read_b64_tr_b16: in each 16-lane group, lane 4a + b points at row
+// a, columns 4b .. 4b+3 of a 4 x 16 block, and lane t receives column t,
+// rows 0..3.  Two reads (rows k .. k+3, k+4 .. k+7) make one operand; the
+// swizzle keeps the 32 lanes of a read on distinct banks.
+__device__ __forceinline__ int vswz(int r) {
+  const int v = (r >> 1) & 7;
+  return ((v & 1) << 2) | (v & 2) | (v >> 2);
+}
+__device__ __forceinline__ int vchunk(int r, int c) { return r * kD + ((c ^ vswz(r)) << 3); }
+__device__ __forceinline__ half4 lds_tr4(const half_t* p) {
+  typedef short short4v __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) short4v lds_short4;
+  const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(const_cast<half_t*>(p)));
+  return __builtin_bit_cast(half4, v);
+}
+// A lane's transpose-read offset (halfs) in a V-rows tile for operand rows
+// d = 32 mh .. 32 mh + 31 (d = lane % 32 + 32 mh), keys 8(lane/32) + 4 hi ..
+__device__ __forceinline__ int vtr_offset(int lane, int mh, int hi) {
+  const int row = 8 * (lane >> 5) + ((lane & 15) >> 2) + 4 * hi;
+  const int col = 32 * mh + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  return vchunk(row, col >> 3) + (col & 7);
+}
+
+template <int NW, int GW, bool VT_VEC, bool VROWS>
 __global__ void __launch_bounds__(64 * NW, 8 / NW)
 sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
                  const half_t* __restrict__ Vt, half_t* __restrict__ O, float* __restrict__ L,
@@ -189,6 +215,7 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
   const int cr = tid >> 3, cc = tid & 7;
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<half_t*>(K + (size_t)kv * T * kD), 0, T * kD * 2, kBufferWord3);
+  // V^T of head kv, or (VROWS) V rows of head kv: the same element count
   const half_t* Vh = Vt + (size_t)kv * kD * T;
   const __amdgpu_buffer_rsrc_t vrsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(Vh), 0, kD * T * 2, kBufferWord3);
@@ -210,7 +237,11 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
 #pragma unroll
     for (int p = 0; p < kCpt; ++p) {
       const int rb = vByte + p * kRowsPerPass * T * 2;
-      if (VT_VEC) {
+      if (VROWS) {  // rows past T read as zeros, like K's
+        dst[p] = __builtin_amdgcn_raw_buffer_load_b128(
+            vrsrc, kByte + p * kRowsPerPass * kD * 2,
+            __builtin_amdgcn_readfirstlane(kt * kBN * kD * 2), 0);
+      } else if (VT_VEC) {
         const int off = key0 + cc * 8 < T ? rb : kOutOfRange;
         dst[p] = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off,
                                                        __builtin_amdgcn_readfirstlane(key0 * 2), 0);
@@ -236,14 +267,35 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
   auto store_v = [&](int buf, const Stage& src) {
     const int b = __builtin_amdgcn_readfirstlane(buf * kTileBytes);
 #pragma unroll
-    for (int p = 0; p < kCpt; ++p)
-      *reinterpret_cast<int4v*>(reinterpret_cast<char*>(vring) + b +
-                                (stOff + p * kRowsPerPass * kRowHalfs) * 2) = src[p];
+    for (int p = 0; p < kCpt; ++p) {
+      const int off = VROWS ? vchunk(cr + p * kRowsPerPass, cc) : stOff + p * kRowsPerPass * kRowHalfs;
+      *reinterpret_cast<int4v*>(reinterpret_cast<char*>(vring) + b + off * 2) = src[p];
+    }
   };
 
   const int swapAddr = (lane ^ 32) << 2;
   const int kOff = krow(n) * kRowHalfs + 8 * g;
   const int vOff = n * kRowHalfs + 8 * g;
+  int vtrOff[2][2];  // VROWS: transpose-read offsets, d rows 32 mh .., keys 4 hi ..
+#pragma unroll
+  for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) vtrOff[mh][hi] = VROWS ? vtr_offset(lane, mh, hi) : 0;
+  // V^T operand of P V from ring buffer `buf`: keys 16 ks4 + 8g .. +7 of the
+  // tile, d rows 32 mh + n; from a V^T tile (one 16-byte read) or, with
+  // VROWS, from a V-rows tile (two transpose reads)
+  auto vt_operand = [&](int buf, int ks4, int mh) -> half8 {
+    if constexpr (VROWS) {
+      const half_t* base = reinterpret_cast<const half_t*>(
+          reinterpret_cast<const char*>(vring) + __builtin_amdgcn_readfirstlane(buf * kTileBytes)) +
+          16 * ks4 * kD;
+      const half4 lo = lds_tr4(base + vtrOff[mh][0]);
+      const half4 hi = lds_tr4(base + vtrOff[mh][1]);
+      return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      return lds8(vring, buf, vOff * 2, (32 * mh * kRowHalfs + 16 * ks4) * 2);
+    }
+  };
 
 #pragma nounroll
   for (int task = 0; task < 2; ++task) {
@@ -279,8 +331,8 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
     auto pv = [&](int buf, const half8 (&p)[4]) {
 #pragma unroll
       for (int ks4 = 0; ks4 < 4; ++ks4) {
-        const half8 v0 = lds8(vring, buf, vOff * 2, 32 * ks4);
-        const half8 v1 = lds8(vring, buf, vOff * 2, (32 * kRowHalfs + 16 * ks4) * 2);
+        const half8 v0 = vt_operand(buf, ks4, 0);
+        const half8 v1 = vt_operand(buf, ks4, 1);
         o0 = mfma(v0, p[ks4], o0);
         o1 = mfma(v1, p[ks4], o1);
       }
@@ -333,7 +385,7 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
       const int vbuf = (j + kVRing - 1) % kVRing, kbuf = (j + 1) % kKRing;
       auto rd = [&](int i) -> half8 {
         if (i < 8)  // V^T operand of P V: slice ks4 = i/2, d rows 32*(i%2)
-          return lds8(vring, vbuf, vOff * 2, (32 * (i & 1) * kRowHalfs + 16 * (i >> 1)) * 2);
+          return vt_operand(vbuf, i >> 1, i & 1);
         const int kk = (i - 8) >> 1, sb = i & 1;  // K operand of S: k-step kk, key rows 32*sb
         return lds8(kring, kbuf, kOff * 2, (32 * sb * kRowHalfs + 16 * kk) * 2);
       };
@@ -556,7 +608,7 @@ int check_device() {
   return ok ? SATTN_OK : SATTN_ERR_DEVICE;
 }
 
-template <int NW, int GW, bool VT_VEC>
+template <int NW, int GW, bool VT_VEC, bool VROWS>
 void launch(const half_t* Q, const half_t* K, const half_t* Vt, half_t* O, float* L, float c,
             int T, int Hq, int Hkv, hipStream_t stream) {
   constexpr int RS = NW / GW;
@@ -566,53 +618,69 @@ void launch(const half_t* Q, const half_t* K, const half_t* Vt, half_t* O, float
   const int nSlotGroups = (nPairs + RS - 1) / RS;
   const int nHeadGroups = G / GW;
   const unsigned grid = (unsigned)nSlotGroups * (unsigned)Hkv * (unsigned)nHeadGroups;
-  hipLaunchKernelGGL((sattn_fwd_kernel<NW, GW, VT_VEC>), dim3(grid), dim3(64 * NW), 0, stream, Q,
-                     K, Vt, O, L, c, T, Hq, Hkv, G, nBlocks, nPairs, nSlotGroups, nHeadGroups);
+  hipLaunchKernelGGL((sattn_fwd_kernel<NW, GW, VT_VEC, VROWS>), dim3(grid), dim3(64 * NW), 0,
+                     stream, Q, K, Vt, O, L, c, T, Hq, Hkv, G, nBlocks, nPairs, nSlotGroups,
+                     nHeadGroups);
 }
 
 // Eight-wave workgroups (one per CU) feed each K/V tile to twice the query
 // rows; when they would leave CUs idle, four-wave workgroups (two per CU)
 // double the number of workgroups.
-template <int GW, bool VT_VEC>
+template <int GW, bool VT_VEC, bool VROWS>
 void launch_nw(const half_t* Q, const half_t* K, const half_t* Vt, half_t* O, float* L, float c,
                int T, int Hq, int Hkv, hipStream_t stream) {
   const int nPairs = ((T + 31) / 32 + 1) / 2;
   const long long grid8 =
       (long long)((nPairs + 8 / GW - 1) / (8 / GW)) * Hkv * ((Hq / Hkv) / GW);
   if (grid8 >= kCus)
-    launch<8, GW, VT_VEC>(Q, K, Vt, O, L, c, T, Hq, Hkv, stream);
+    launch<8, GW, VT_VEC, VROWS>(Q, K, Vt, O, L, c, T, Hq, Hkv, stream);
   else
-    launch<4, GW, VT_VEC>(Q, K, Vt, O, L, c, T, Hq, Hkv, stream);
+    launch<4, GW, VT_VEC, VROWS>(Q, K, Vt, O, L, c, T, Hq, Hkv, stream);
 }
 
-template <int GW>
-void launch_gw(const half_t* Q, const half_t* K, const half_t* Vt, half_t* O, float* L, float c,
+// V^T chunks of 8 keys are whole 16-byte loads only when T % 8 == 0; V rows
+// are always whole 128-byte rows.
+template <int GW, bool VROWS>
+void launch_gw(const half_t* Q, const half_t* K, const half_t* V, half_t* O, float* L, float c,
                int T, int Hq, int Hkv, hipStream_t stream) {
-  if (T % 8 == 0)
-    launch_nw<GW, true>(Q, K, Vt, O, L, c, T, Hq, Hkv, stream);
+  if (VROWS)
+    launch_nw<GW, false, true>(Q, K, V, O, L, c, T, Hq, Hkv, stream);
+  else if (T % 8 == 0)
+    launch_nw<GW, true, false>(Q, K, V, O, L, c, T, Hq, Hkv, stream);
   else
-    launch_nw<GW, false>(Q, K, Vt, O, L, c, T, Hq, Hkv, stream);
+    launch_nw<GW, false, false>(Q, K, V, O, L, c, T, Hq, Hkv, stream);
+}
+
+template <bool VROWS>
+int forward(const void* Q, const void* K, const void* V, void* O, float* L, float c, int T,
+            int Hq, int Hkv, void* stream) {
+  const int st = sattn_fwd_check(Q, K, V, O, L, c, T, Hq, Hkv);
+  if (st != SATTN_OK) return st;
+  const int dst = check_device();
+  if (dst != SATTN_OK) return dst;
+  const half_t* q = static_cast<const half_t*>(Q);
+  const half_t* k = static_cast<const half_t*>(K);
+  const half_t* v = static_cast<const half_t*>(V);
+  half_t* o = static_cast<half_t*>(O);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int G = Hq / Hkv;
+  if (G % 4 == 0)
+    launch_gw<4, VROWS>(q, k, v, o, L, c, T, Hq, Hkv, s);
+  else if (G % 2 == 0)
+    launch_gw<2, VROWS>(q, k, v, o, L, c, T, Hq, Hkv, s);
+  else
+    launch_gw<1, VROWS>(q, k, v, o, L, c, T, Hq, Hkv, s);
+  return hipGetLastError() == hipSuccess ? SATTN_OK : SATTN_ERR_LAUNCH;
 }
 
 }  // namespace
 
 extern "C" int sattn_fwd(const void* Q, const void* K, const void* Vt, void* O, float* L,
                          float c, int T, int Hq, int Hkv, void* stream) {
-  const int st = sattn_fwd_check(Q, K, Vt, O, L, c, T, Hq, Hkv);
-  if (st != SATTN_OK) return st;
-  const int dst = check_device();
-  if (dst != SATTN_OK) return dst;
-  const half_t* q = static_cast<const half_t*>(Q);
-  const half_t* k = static_cast<const half_t*>(K);
-  const half_t* v = static_cast<const half_t*>(Vt);
-  half_t* o = static_cast<half_t*>(O);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int G = Hq / Hkv;
-  if (G % 4 == 0)
-    launch_gw<4>(q, k, v, o, L, c, T, Hq, Hkv, s);
-  else if (G % 2 == 0)
-    launch_gw<2>(q, k, v, o, L, c, T, Hq, Hkv, s);
-  else
-    launch_gw<1>(q, k, v, o, L, c, T, Hq, Hkv, s);
-  return hipGetLastError() == hipSuccess ? SATTN_OK : SATTN_ERR_LAUNCH;
+  return forward<false>(Q, K, Vt, O, L, c, T, Hq, Hkv, stream);
+}
+
+extern "C" int sattn_fwd_vrows(const void* Q, const void* K, const void* V, void* O, float* L,
+                               float c, int T, int Hq, int Hkv, void* stream) {
+  return forward<true>(Q, K, V, O, L, c, T, Hq, Hkv, stream);
 }

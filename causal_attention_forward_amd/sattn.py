@@ -44,6 +44,8 @@ _lib.sattn_fwd.restype = ctypes.c_int
 _lib.sattn_fwd.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                            ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                            ctypes.c_int, ctypes.c_void_p]
+_lib.sattn_fwd_vrows.restype = ctypes.c_int
+_lib.sattn_fwd_vrows.argtypes = _lib.sattn_fwd.argtypes
 _lib.sattn_fwd_check.restype = ctypes.c_int
 _lib.sattn_fwd_check.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
@@ -77,7 +79,7 @@ SATTN_ERR_LAUNCH = 7
 SATTN_ERR_WORKSPACE = 8
 HEAD_DIM = 64
 
-EXPORTS = ("sattn_fwd", "sattn_fwd_check", "sattn_status_string", "sattn_bwd_query",
+EXPORTS = ("sattn_fwd", "sattn_fwd_vrows", "sattn_fwd_check", "sattn_status_string", "sattn_bwd_query",
            "sattn_bwd_key", "sattn_bwd", "sattn_bwd_workspace_bytes", "sattn_bwd_check",
            "sattn_bwd_query_check", "sattn_bwd_key_check")
 
@@ -98,10 +100,44 @@ def sattn_fwd(Q: int, K: int, Vt: int, O: int, L: int, c: float, T: int, Hq: int
     return _lib.sattn_fwd(Q, K, Vt, O, L, ctypes.c_float(c), T, Hq, Hkv, stream)
 
 
+def sattn_fwd_vrows(Q: int, K: int, V: int, O: int, L: int, c: float, T: int, Hq: int, Hkv: int,
+                    stream: int | None = None) -> int:
+    """The C entry point taking V as rows [Hkv][T][64]; returns the status code."""
+    return _lib.sattn_fwd_vrows(Q, K, V, O, L, ctypes.c_float(c), T, Hq, Hkv, stream)
+
+
 def sattn_fwd_check(Q: int, K: int, Vt: int, O: int, L: int, c: float, T: int, Hq: int,
                     Hkv: int) -> int:
     """Host-side validation only (no HIP call); returns the status code."""
     return _lib.sattn_fwd_check(Q, K, Vt, O, L, ctypes.c_float(c), T, Hq, Hkv)
+
+
+def fwd_vrows(q, k, v, c, out=None, lse=None, stream=None):
+    """As ``fwd`` with V given as rows: v float16 [Hkv][T][64] (no V^T needed)."""
+    import torch
+
+    Hq, T, D = q.shape
+    Hkv = k.shape[0]
+    if D != HEAD_DIM or tuple(k.shape) != (Hkv, T, D) or tuple(v.shape) != (Hkv, T, D):
+        raise ValueError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        if x.dtype != torch.float16 or not x.is_cuda or not x.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float16 GPU tensor")
+    if out is None:
+        out = torch.empty((T, Hq * D), dtype=torch.float16, device=q.device)
+    if lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    if (out.dtype != torch.float16 or lse.dtype != torch.float32 or not out.is_contiguous()
+            or not lse.is_contiguous() or out.numel() != T * Hq * D or lse.numel() != Hq * T):
+        raise ValueError("out must be contiguous float16 [T][Hq*64], lse contiguous float32 [Hq][T]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        st = sattn_fwd_vrows(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), float(c), T, Hq, Hkv, stream.cuda_stream)
+    if st != SATTN_OK:
+        raise SattnError(st)
+    return out, lse
 
 
 def fwd(q, k, vt, c, out=None, lse=None, stream=None):

@@ -75,6 +75,19 @@ int sattn_fwd(const void* Q, const void* K, const void* Vt, void* O, float* L,
               float c, int T, int Hq, int Hkv, void* stream);
 
 /*
+ * sattn_fwd_vrows: sattn_fwd with V given as rows, binary16 [Hkv][T][64]
+ * (V of K/V head kv, token j at (kv*T + j)*64), the layout the value
+ * projection produces, instead of V^T; everything else, the results
+ * included, is as for sattn_fwd (bit-identical O and L for the same values).
+ * It removes the value-transpose step before the attention (StreamingAttention
+ * head-layout page, value-transpose; Graph page, cgLayerForwardWith): the
+ * kernel reads the V^T operand of P V from row-major V tiles with the gfx950
+ * LDS transpose read.  V must be 16-byte aligned; validation as sattn_fwd.
+ */
+int sattn_fwd_vrows(const void* Q, const void* K, const void* V, void* O, float* L, float c,
+                    int T, int Hq, int Hkv, void* stream);
+
+/*
  * sattn_fwd_check: the host-side argument validation of sattn_fwd alone
  * (the admission rule of the StreamingAttentionSM86 page, with T no longer
  * required to be a multiple of 64, plus pointer checks).  Makes no HIP call,

@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "sattn_fwd", "sattn_fwd_check", "sattn_status_string", "sattn_bwd", "sattn_bwd_check",
+        "sattn_fwd", "sattn_fwd_vrows", "sattn_fwd_check", "sattn_status_string", "sattn_bwd",
+        "sattn_bwd_check",
         "sattn_bwd_key", "sattn_bwd_key_check", "sattn_bwd_query", "sattn_bwd_query_check",
         "sattn_bwd_workspace_bytes"])
 
@@ -130,6 +131,9 @@ def test_entry_point_validates_before_any_device_call(sattn):
     assert sattn.sattn_fwd(Qa, Ka, Va, Oa, La, C, 0, HQ, HKV, None) == sattn.SATTN_ERR_SHAPE
     assert sattn.sattn_fwd(Qa, Ka, Va, Oa, La, -1.0, T, HQ, HKV, None) == sattn.SATTN_ERR_SCALE
     assert sattn.sattn_fwd(Qa, Ka, Va, Qa, La, C, T, HQ, HKV, None) == sattn.SATTN_ERR_ALIAS
+    assert sattn.sattn_fwd_vrows(None, Ka, Va, Oa, La, C, T, HQ, HKV, None) == sattn.SATTN_ERR_NULL
+    assert sattn.sattn_fwd_vrows(Qa, Ka, Va + 8, Oa, La, C, T, HQ, HKV, None) == sattn.SATTN_ERR_ALIGN
+    assert sattn.sattn_fwd_vrows(Qa, Ka, Va, Va, La, C, T, HQ, HKV, None) == sattn.SATTN_ERR_ALIAS
 
 
 def test_product_path_has_no_oracle_or_fallback():
