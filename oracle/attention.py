@@ -95,3 +95,27 @@ def attention_rows_ref(Q, K, Vt, c, h: int, rows):
         O[n] = (Vt[kv, :, :i + 1].astype(np.float64) @ w) / Z
         L[n] = M + np.log2(Z)
     return O, L
+
+
+def materialised_rows_ref(Q, K, Vt, c, h: int, rows):
+    """The materialised path's intermediate planes for selected rows of head h.
+
+    Returns ``(S_rows, P_rows)``, float64 ``[len(rows)][T]``: the base-2 scores
+    S_ij = c (q_i . k_j) and the causal softmax probabilities
+    P_ij = 2^(S_ij - M_i) / sum_j' 2^(S_ij' - M_i) for keys j <= i (M_i the row
+    maximum); entries with j > i are -inf and 0.  O = P V and L = M + log2 of
+    that sum are ``attention_ref``'s results for the same rows.
+    """
+    Q, K, Vt, Hq, Hkv, T = _check(Q, K, Vt)
+    kv = h // (Hq // Hkv)
+    c = float(c)
+    rows = list(rows)
+    S = np.full((len(rows), T), -np.inf)
+    P = np.zeros((len(rows), T))
+    k = K[kv].astype(np.float64)
+    for n, i in enumerate(rows):
+        t = (k[:i + 1] @ Q[h, i].astype(np.float64)) * c
+        w = np.exp2(t - t.max())
+        S[n, :i + 1] = t
+        P[n, :i + 1] = w / w.sum()
+    return S, P

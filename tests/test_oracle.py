@@ -332,3 +332,37 @@ def test_inputs_recipe():
         assert (means[kv] > 2.0).sum() == math.ceil(w.peaked_fraction * w.T)
     z = make_workload(4)
     assert 1.4 < z.Q.astype(np.float64).std() < 1.6 and 0.95 < z.Vt.astype(np.float64).std() < 1.05
+
+
+# --------------------------------------------------------------------------
+# the materialised path's planes (scores and probabilities)
+# --------------------------------------------------------------------------
+def test_materialised_rows_pins():
+    """The scores against exact rational products (T=6); the probabilities sum
+    to one, vanish above the diagonal, reproduce O = P V and L = log2 sum 2^S of
+    the pinned attention_ref, and are monotone in the scores."""
+    from oracle import materialised_rows_ref
+    x = make_inputs(6, 2, 1, seed=26, qk_std=1.5)
+    S, P = materialised_rows_ref(x.Q, x.K, x.Vt, x.c, 1, range(6))
+    cf = Fraction(float(x.c))
+    for i in range(6):
+        for j in range(6):
+            if j > i:
+                assert S[i, j] == -np.inf and P[i, j] == 0.0
+                continue
+            exact = cf * sum(Fraction(float(x.Q[1, i, d])) * Fraction(float(x.K[0, j, d]))
+                             for d in range(64))
+            assert abs(S[i, j] - float(exact)) <= 1e-12 * max(1.0, abs(float(exact)))
+    y = make_inputs(300, 4, 2, seed=27, peaked_fraction=0.02)
+    O, L = attention_ref(y.Q, y.K, y.Vt, y.c)
+    rows = [0, 1, 63, 64, 150, 299]
+    for h in (0, 3):
+        S, P = materialised_rows_ref(y.Q, y.K, y.Vt, y.c, h, rows)
+        assert np.allclose(P.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+        V = y.Vt[h // 2].astype(np.float64).T
+        assert np.allclose(P @ V, O[rows, h * 64:(h + 1) * 64], rtol=0, atol=1e-12)
+        for n, i in enumerate(rows):
+            t = S[n, :i + 1]
+            assert abs(np.log2(np.exp2(t - t.max()).sum()) + t.max() - L[h, i]) <= 1e-12
+            order = np.argsort(t)
+            assert np.all(np.diff(P[n, :i + 1][order]) >= 0)
