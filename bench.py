@@ -205,6 +205,105 @@ def bench_backward(args, torch, sattn, x, w):
     print(json.dumps(out), flush=True)
 
 
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+
+
+def bench_materialized(args, torch, sattn, x, w):
+    """The --materialized line: the whole path per step, each launch alone
+    (HIP events on the stream), and the streaming forward on the same inputs."""
+    dev = torch.device("cuda:0")
+    T, Hq, Hkv = x.T, x.Hq, x.Hkv
+    q = torch.from_numpy(x.Q).to(dev)
+    k = torch.from_numpy(x.K).to(dev)
+    vt = torch.from_numpy(x.Vt).to(dev)
+    S = torch.empty((Hq, T, T), dtype=torch.float32, device=dev)
+    P = torch.empty((Hq, T, T), dtype=torch.float16, device=dev)
+    O = torch.empty((T, Hq * 64), dtype=torch.float16, device=dev)
+    L = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    c = float(x.c)
+    ptr = lambda t: t.data_ptr()  # noqa: E731
+
+    def check(st):
+        assert st == sattn.SATTN_OK, sattn.sattn_status_string(st)
+
+    def step():
+        check(sattn.sattn_mat_fwd(ptr(q), ptr(k), ptr(vt), ptr(O), ptr(L), ptr(S), ptr(P), c, T,
+                                  Hq, Hkv, sp))
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    n = max(args.steps // 2, 1)
+    ms = {
+        "scores_ms": timed(lambda: check(sattn.sattn_mat_scores(ptr(q), ptr(k), ptr(S), c, T, Hq,
+                                                                 Hkv, sp)), n),
+        "softmax_ms": timed(lambda: check(sattn.sattn_mat_softmax(ptr(S), ptr(P), ptr(L), T, Hq,
+                                                                   sp)), n),
+        "pv_ms": timed(lambda: check(sattn.sattn_mat_pv(ptr(P), ptr(vt), ptr(O), T, Hq, Hkv,
+                                                         sp)), n),
+    }
+
+    def streaming():
+        check(sattn.sattn_fwd(ptr(q), ptr(k), ptr(vt), ptr(O), ptr(L), c, T, Hq, Hkv, sp))
+
+    timed(streaming, max(args.warmup, 100))   # its own warmup after the plane-bound launches
+    ms["streaming_fwd_ms"] = timed(streaming, max(args.steps, 200))
+    tri = Hq * T * (T + 1) // 2            # plane elements with j <= i
+    bytes_ = {                             # algorithmic HBM bytes per launch
+        "scores_ms": 4 * tri + 2 * 64 * T * (Hq + Hkv),
+        "softmax_ms": 4 * tri + 2 * tri + 4 * Hq * T,
+        "pv_ms": 2 * tri + 2 * 64 * T * (Hq + Hkv),
+    }
+    dom = max(bytes_, key=lambda k_: ms[k_])
+    gbs = bytes_[dom] / (ms[dom] * 1e-3) / 1e9
+    flops = causal_flops(T, Hq)
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": f"causal attn fwd TFLOP/s, materialised path (scores plane, softmax, P V), "
+                  f"T={T} Hq={Hq} Hkv={Hkv} d=64",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": w.name + " materialised", "T": T, "Hq": Hq, "Hkv": Hkv,
+                   "head_dim": 64, "causal": True, "flop_per_call": flops,
+                   "plane_bytes": 6 * Hq * T * T,
+                   **{k_: round(v_, 5) for k_, v_ in ms.items()},
+                   "streaming_speedup": round(ms_per_step / ms["streaming_fwd_ms"], 2)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": dom.replace("_ms", ""), "algorithmic_bytes": bytes_[dom],
+                     "kernel_ms": round(ms[dom], 5)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
 def compulsory_bytes(T, Hq, Hkv, d=64):
     """Q, K and V^T read once, O and L written once."""
     return 2 * d * T * (Hq + 2 * Hkv) + 2 * d * T * Hq + 4 * T * Hq
@@ -270,6 +369,10 @@ def main():
                          "(median of 5 timed runs, input sets rotated so small ones are not cache figures)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (sattn_bwd) instead of the forward")
+    ap.add_argument("--materialized", action="store_true",
+                    help="time the materialised path (scores plane, causal softmax, P V) instead")
+    ap.add_argument("--workload", type=int, default=WORKLOAD_INDEX,
+                    help="index of the synthetic workload (default: the T=4096 Hq=32 Hkv=8 one)")
     ap.add_argument("--vrows", action="store_true",
                     help="time the forward taking V as rows (sattn_fwd_vrows) instead of V^T")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -301,8 +404,11 @@ def main():
         sweep(torch, sattn, WORKLOADS, make_workload)
         return
 
-    w = WORKLOADS[WORKLOAD_INDEX]
-    x = make_workload(WORKLOAD_INDEX)
+    w = WORKLOADS[args.workload]
+    x = make_workload(args.workload)
+    if args.materialized:
+        bench_materialized(args, torch, sattn, x, w)
+        return
     if args.backward:
         bench_backward(args, torch, sattn, x, w)
         return

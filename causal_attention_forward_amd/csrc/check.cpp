@@ -160,6 +160,93 @@ extern "C" int sattn_bwd_key_check(const void* Q, const void* K, const void* Vt,
   return check_bwd(a, false, true);
 }
 
+extern "C" int sattn_mat_fwd_check(const void* Q, const void* K, const void* Vt, const void* O,
+                                   const float* L, const float* S, const void* P, float c, int T,
+                                   int Hq, int Hkv) {
+  if (!Q || !K || !Vt || !O || !L || !S || !P) return SATTN_ERR_NULL;
+  const int st = check_shape_scale(c, T, Hq, Hkv);
+  if (st != SATTN_OK) return st;
+  const uint64_t t = static_cast<uint64_t>(T);
+  const uint64_t hq = static_cast<uint64_t>(Hq), hkv = static_cast<uint64_t>(Hkv);
+  const uint64_t plane = hq * t * t;  // elements of S and of P
+  if (plane * 4u > (1ull << 40)) return SATTN_ERR_SHAPE;
+  if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(Vt, 16) || misaligned(O, 16) ||
+      misaligned(S, 16) || misaligned(P, 16) || misaligned(L, 4))
+    return SATTN_ERR_ALIGN;
+  const uint64_t half = t * SATTN_HEAD_DIM * 2u;
+  const Span in[3] = {span(Q, hq * half), span(K, hkv * half), span(Vt, hkv * half)};
+  const Span out[4] = {span(O, hq * half), span(L, hq * t * 4u), span(S, plane * 4u),
+                       span(P, plane * 2u)};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (overlaps(out[i], in[j])) return SATTN_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(out[i], out[j])) return SATTN_ERR_ALIAS;
+  }
+  return SATTN_OK;
+}
+
+namespace {
+
+int mat_shape(int T, int Hq, int Hkv) {
+  const int st = check_shape_scale(1.0f, T, Hq, Hkv);
+  if (st != SATTN_OK) return st;
+  const uint64_t t = static_cast<uint64_t>(T);
+  if (static_cast<uint64_t>(Hq) * t * t * 4u > (1ull << 40)) return SATTN_ERR_SHAPE;
+  return SATTN_OK;
+}
+
+int disjoint(const Span* in, int nIn, const Span* out, int nOut) {
+  for (int i = 0; i < nOut; ++i) {
+    for (int j = 0; j < nIn; ++j)
+      if (overlaps(out[i], in[j])) return SATTN_ERR_ALIAS;
+    for (int j = i + 1; j < nOut; ++j)
+      if (overlaps(out[i], out[j])) return SATTN_ERR_ALIAS;
+  }
+  return SATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int sattn_mat_scores_check(const void* Q, const void* K, const float* S, float c,
+                                      int T, int Hq, int Hkv) {
+  if (!Q || !K || !S) return SATTN_ERR_NULL;
+  int st = mat_shape(T, Hq, Hkv);
+  if (st != SATTN_OK) return st;
+  if (!isfinite(c) || !(c > 0.0f)) return SATTN_ERR_SCALE;
+  if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(S, 16)) return SATTN_ERR_ALIGN;
+  const uint64_t t = static_cast<uint64_t>(T), half = t * SATTN_HEAD_DIM * 2u;
+  const Span in[2] = {span(Q, static_cast<uint64_t>(Hq) * half),
+                      span(K, static_cast<uint64_t>(Hkv) * half)};
+  const Span out[1] = {span(S, static_cast<uint64_t>(Hq) * t * t * 4u)};
+  return disjoint(in, 2, out, 1);
+}
+
+extern "C" int sattn_mat_softmax_check(const float* S, const void* P, const float* L, int T,
+                                       int Hq) {
+  if (!S || !P || !L) return SATTN_ERR_NULL;
+  int st = mat_shape(T, Hq, 1);
+  if (st != SATTN_OK) return st;
+  if (misaligned(S, 16) || misaligned(P, 16) || misaligned(L, 4)) return SATTN_ERR_ALIGN;
+  const uint64_t t = static_cast<uint64_t>(T), plane = static_cast<uint64_t>(Hq) * t * t;
+  const Span in[1] = {span(S, plane * 4u)};
+  const Span out[2] = {span(P, plane * 2u), span(L, static_cast<uint64_t>(Hq) * t * 4u)};
+  return disjoint(in, 1, out, 2);
+}
+
+extern "C" int sattn_mat_pv_check(const void* P, const void* Vt, const void* O, int T, int Hq,
+                                  int Hkv) {
+  if (!P || !Vt || !O) return SATTN_ERR_NULL;
+  int st = mat_shape(T, Hq, Hkv);
+  if (st != SATTN_OK) return st;
+  if (misaligned(P, 16) || misaligned(Vt, 16) || misaligned(O, 16)) return SATTN_ERR_ALIGN;
+  const uint64_t t = static_cast<uint64_t>(T), half = t * SATTN_HEAD_DIM * 2u;
+  const Span in[2] = {span(P, static_cast<uint64_t>(Hq) * t * t * 2u),
+                      span(Vt, static_cast<uint64_t>(Hkv) * half)};
+  const Span out[1] = {span(O, static_cast<uint64_t>(Hq) * half)};
+  return disjoint(in, 2, out, 1);
+}
+
 extern "C" const char* sattn_status_string(int status) {
   switch (status) {
     case SATTN_OK: return "ok";

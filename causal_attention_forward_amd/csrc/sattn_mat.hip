@@ -1,0 +1,391 @@
+// The materialised causal attention for gfx950 (CDNA4): the baseline the
+// streaming forward avoids, with its C entry.
+//
+// What it computes (the pages' materialised path: the Graph page's scores
+// plane, cgScores / cgScoresBytes, 4 H T^2 bytes, and its binary16 variant;
+// the causal softmax device image of the Coppelius device-image page; the
+// StreamingAttentionSM86 page's note that the materialised path rounds its
+// probabilities to binary16 before their product with V):
+//   1. scores:  S[h][i][j] = c (q_i . k_j), binary32, base-2 units, for j <= i;
+//   2. softmax: L[h][i] = log2 sum_{j<=i} 2^S[h][i][j] and the probabilities
+//      P[h][i][j] = 2^(S[h][i][j] - L[h][i]) rounded to binary16;
+//   3. P V:     O[i][h*64 + d] = sum_{j<=i} P[h][i][j] V[j][d], binary32 sums,
+//      rounded to binary16 (token-major, like the streaming forward's O).
+// The planes hold T x T per head, so this path moves about 10 H T^2 bytes
+// through HBM where the streaming forward moves the inputs and outputs only.
+//
+// gfx950 design:
+//  * Scores: one workgroup per 64 x 64 tile on or below the diagonal (tiles
+//    above it are never touched), four waves of 32 x 32, each one
+//    v_mfma_f32_32x32x16_f16 chain over the 64 head-width columns with its
+//    operands straight from global memory (16-byte rows of Q and K).  In the
+//    accumulator a lane holds one key column, so the 32 lanes of a row store
+//    128 consecutive bytes.
+//  * Softmax: one wave per row, 4-float reads per lane; the row (up to 4096
+//    keys) stays in registers while a running maximum and sum per lane are
+//    merged across the wave, then P is written from the registers, so S is
+//    read once; longer rows are read twice.  HBM-bound.
+//  * P V: a workgroup takes 128 query rows of a head (a wave 32 rows x all
+//    64 columns) and stages each 64-key V^T tile in LDS once for its four
+//    waves; P rows are 16-byte reads straight from global memory.  Keys past
+//    the row (only in the diagonal tile) are masked in registers, so the
+//    planes' memory above the diagonal is never read into a result.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "sattn.h"
+
+namespace {
+
+typedef _Float16 half_t;
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+
+constexpr int kD = SATTN_HEAD_DIM;
+
+__device__ __forceinline__ float16v mfma(half8 a, half8 b, float16v c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ half8 ld8(const half_t* p) { return *reinterpret_cast<const half8*>(p); }
+
+// -------------------------------------------------------------------------
+// 1. scores.  Grid (nt (nt+1) / 2 lower-triangle 64 x 64 tiles, Hq), 256
+// threads: wave w computes the 32 x 32 block (w / 2, w % 2) of its tile.
+// -------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+sattn_mat_scores_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
+                        float* __restrict__ S, float c, int T, int G) {
+  const int tile = blockIdx.x, h = blockIdx.y, kv = h / G;
+  // tile = it (it + 1) / 2 + jt with 0 <= jt <= it
+  int it = (int)((sqrtf(8.0f * (float)tile + 1.0f) - 1.0f) * 0.5f);
+  while ((it + 1) * (it + 2) / 2 <= tile) ++it;
+  while (it * (it + 1) / 2 > tile) --it;
+  const int jt = tile - it * (it + 1) / 2;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
+  const int i0 = it * 64 + 32 * (wave >> 1), j0 = jt * 64 + 32 * (wave & 1);
+  if (j0 > i0 + 31) return;  // a 32 x 32 block wholly above the diagonal
+  const int ia = i0 + n, jb = j0 + n;
+  float16v acc = {};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const half8 z = {};
+    const half8 a = ia < T ? ld8(Q + ((size_t)h * T + ia) * kD + 16 * kk + 8 * g) : z;
+    const half8 b = jb < T ? ld8(K + ((size_t)kv * T + jb) * kD + 16 * kk + 8 * g) : z;
+    acc = mfma(a, b, acc);
+  }
+  // element r of lane (n, g): query i0 + 8(r/4) + 4g + r%4, key jb
+  if (jb < T) {
+    float* col = S + (size_t)h * T * T + jb;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = i0 + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (i < T && jb <= i) col[(size_t)i * T] = acc[r] * c;
+    }
+  }
+}
+
+// -------------------------------------------------------------------------
+// 2. causal softmax.  One wave per row (h, i): 64 lanes x 4 keys per chunk.
+// -------------------------------------------------------------------------
+__device__ __forceinline__ void merge(float& m, float& l, float m2, float l2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;  // both empty
+  l = l * __builtin_amdgcn_exp2f(m - mn) + l2 * __builtin_amdgcn_exp2f(m2 - mn);
+  m = mn;
+}
+
+// Rows of at most 64 * 4 * NCH keys: the row stays in registers between the
+// two passes, so S is read from HBM once.  NCH = 0: any length, two reads.
+template <bool VEC, int NCH>
+__global__ void __launch_bounds__(256)
+sattn_mat_softmax_kernel(const float* __restrict__ S, half_t* __restrict__ P,
+                         float* __restrict__ L, int T, int rows) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int i = row % T;
+  const int cnt = i + 1;  // keys 0..i
+  const float* s = S + (size_t)row * T;
+  half_t* p = P + (size_t)row * T;
+  float m = -INFINITY, l = 0.0f;
+  auto chunk = [&](int base, float (&v)[4]) {
+    const int j = base + 4 * lane;
+    if (VEC && j + 3 < cnt) {
+      const float4v x = *reinterpret_cast<const float4v*>(s + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = x[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = j + e < cnt ? s[j + e] : -INFINITY;
+    }
+  };
+  auto fold = [&](const float (&v)[4]) {
+    const float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+    const float mn = fmaxf(m, mx);
+    if (mn != -INFINITY) {
+      float t = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t += __builtin_amdgcn_exp2f(v[e] - mn);
+      l = l * __builtin_amdgcn_exp2f(m - mn) + t;
+      m = mn;
+    }
+  };
+  auto emit = [&](int base, const float (&v)[4], float lse) {
+    const int j = base + 4 * lane;
+    if (VEC && j + 3 < cnt) {
+      half4 y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = (half_t)__builtin_amdgcn_exp2f(v[e] - lse);
+      *reinterpret_cast<half4*>(p + j) = y;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j + e < cnt) p[j + e] = (half_t)__builtin_amdgcn_exp2f(v[e] - lse);
+    }
+  };
+  float keep[NCH > 0 ? NCH : 1][4];
+  if constexpr (NCH > 0) {
+#pragma unroll
+    for (int cix = 0; cix < NCH; ++cix)
+      if (cix * 256 < cnt) chunk(cix * 256, keep[cix]);
+#pragma unroll
+    for (int cix = 0; cix < NCH; ++cix)
+      if (cix * 256 < cnt) fold(keep[cix]);
+  } else {
+    for (int base = 0; base < cnt; base += 256) {
+      float v[4];
+      chunk(base, v);
+      fold(v);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off, 64);
+    const float l2 = __shfl_xor(l, off, 64);
+    merge(m, l, m2, l2);
+  }
+  const float lse = m + __builtin_amdgcn_logf(l);
+  if constexpr (NCH > 0) {
+#pragma unroll
+    for (int cix = 0; cix < NCH; ++cix)
+      if (cix * 256 < cnt) emit(cix * 256, keep[cix], lse);
+  } else {
+    for (int base = 0; base < cnt; base += 256) {
+      float v[4];
+      chunk(base, v);
+      emit(base, v, lse);
+    }
+  }
+  if (lane == 0) L[row] = lse;
+}
+
+// -------------------------------------------------------------------------
+// 3. P V.  Grid (ceil(T / 128) row blocks, heaviest first; Hq), 256 threads:
+// wave w takes query rows 128 rb + 32 w .. +31 and all 64 head-width
+// columns; the workgroup stages each 64-key V^T tile in LDS once for its four
+// waves (double-buffered), and each wave reads its P rows straight from
+// global memory, four 16-byte reads per tile issued before the products.
+// -------------------------------------------------------------------------
+constexpr int kRowHalfs = kD + 8;  // V^T tile row in LDS: 64 keys + 16 bytes of padding
+constexpr int kTileHalfs = kD * kRowHalfs;
+
+template <bool VEC>
+__global__ void __launch_bounds__(256)
+sattn_mat_pv_kernel(const half_t* __restrict__ P, const half_t* __restrict__ Vt,
+                    half_t* __restrict__ O, int T, int Hq, int G, int nRowBlocks) {
+  __shared__ __attribute__((aligned(16))) half_t vbuf[2 * kTileHalfs];
+  const int h = blockIdx.y, kv = h / G;
+  const int rb = nRowBlocks - 1 - (int)blockIdx.x;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, n = lane & 31, g = lane >> 5;
+  const int row0 = rb * 128;
+  const int i0 = row0 + 32 * wave;
+  const int ia = i0 + n;
+  const int nkt = (min(T, row0 + 128) - 1) / 64 + 1;  // key tiles of the workgroup
+  const half_t* prow = P + ((size_t)h * T + min(ia, T - 1)) * T;
+  const half_t* Vh = Vt + (size_t)kv * kD * T;
+  // staging: thread t owns 16-byte chunks t and t + 256 of a V^T tile
+  // (row d = c / 8, keys 8 (c % 8) ..)
+  const int cr = tid >> 3, cc = tid & 7;
+  half8 st[2];
+  auto load = [&](int kt) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int d = cr + 32 * p, key = kt * 64 + cc * 8;
+      if (VEC && key + 7 < T) {
+        st[p] = ld8(Vh + (size_t)d * T + key);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st[p][e] = key + e < T ? Vh[(size_t)d * T + key + e] : (half_t)0;
+      }
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      *reinterpret_cast<half8*>(vbuf + buf * kTileHalfs + (cr + 32 * p) * kRowHalfs + cc * 8) = st[p];
+  };
+  float16v acc0 = {}, acc1 = {};
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nkt) load(kt + 1);
+    if (kt * 64 <= i0 + 31 && i0 < T) {
+      half8 a[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int ja = kt * 64 + 16 * u + 8 * g;  // this lane's eight keys
+        if (VEC && ia < T && ja + 7 <= ia) {
+          a[u] = ld8(prow + ja);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[u][e] = (ia < T && ja + e <= ia) ? prow[ja + e] : (half_t)0;
+        }
+      }
+      const half_t* vb = vbuf + buf * kTileHalfs + n * kRowHalfs + 8 * g;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc0 = mfma(a[u], ld8(vb + 16 * u), acc0);
+        acc1 = mfma(a[u], ld8(vb + 32 * kRowHalfs + 16 * u), acc1);
+      }
+    }
+    if (kt + 1 < nkt) store(buf ^ 1);
+    __syncthreads();
+  }
+  // element r of lane (n, g): query i0 + 8(r/4) + 4g + r%4, column n (acc0) or 32 + n (acc1)
+  if (i0 < T) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = i0 + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (i < T) {
+        half_t* o = O + (size_t)i * Hq * kD + (size_t)h * kD + n;
+        o[0] = (half_t)acc0[r];
+        o[32] = (half_t)acc1[r];
+      }
+    }
+  }
+}
+
+// Per-device cache of "is gfx950": 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return SATTN_ERR_DEVICE;
+  if (dev < kMaxDevices) {
+    const int cached = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (cached != 0) return cached == 1 ? SATTN_OK : SATTN_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SATTN_ERR_DEVICE;
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? SATTN_OK : SATTN_ERR_DEVICE;
+}
+
+}  // namespace
+
+namespace {
+
+void launch_scores(const half_t* q, const half_t* k, float* S, float c, int T, int Hq, int Hkv,
+                   hipStream_t strm) {
+  const int nt = (T + 63) / 64;
+  const unsigned tiles = (unsigned)nt * (unsigned)(nt + 1) / 2u;
+  hipLaunchKernelGGL(sattn_mat_scores_kernel, dim3(tiles, (unsigned)Hq), dim3(256), 0, strm, q,
+                     k, S, c, T, Hq / Hkv);
+}
+
+template <bool VEC>
+void launch_softmax_vec(const float* S, half_t* p, float* L, int T, int Hq, hipStream_t strm) {
+  const int rows = Hq * T;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (T <= 1024)
+    hipLaunchKernelGGL((sattn_mat_softmax_kernel<VEC, 4>), grid, dim3(256), 0, strm, S, p, L, T,
+                       rows);
+  else if (T <= 4096)
+    hipLaunchKernelGGL((sattn_mat_softmax_kernel<VEC, 16>), grid, dim3(256), 0, strm, S, p, L, T,
+                       rows);
+  else
+    hipLaunchKernelGGL((sattn_mat_softmax_kernel<VEC, 0>), grid, dim3(256), 0, strm, S, p, L, T,
+                       rows);
+}
+
+void launch_softmax(const float* S, half_t* p, float* L, int T, int Hq, hipStream_t strm) {
+  if (T % 4 == 0)
+    launch_softmax_vec<true>(S, p, L, T, Hq, strm);
+  else
+    launch_softmax_vec<false>(S, p, L, T, Hq, strm);
+}
+
+void launch_pv(const half_t* p, const half_t* v, half_t* o, int T, int Hq, int Hkv,
+               hipStream_t strm) {
+  const int nrb = (T + 127) / 128;
+  const dim3 grid((unsigned)nrb, (unsigned)Hq);
+  if (T % 8 == 0)
+    hipLaunchKernelGGL(sattn_mat_pv_kernel<true>, grid, dim3(256), 0, strm, p, v, o, T, Hq,
+                       Hq / Hkv, nrb);
+  else
+    hipLaunchKernelGGL(sattn_mat_pv_kernel<false>, grid, dim3(256), 0, strm, p, v, o, T, Hq,
+                       Hq / Hkv, nrb);
+}
+
+int launched() { return hipGetLastError() == hipSuccess ? SATTN_OK : SATTN_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" int sattn_mat_fwd(const void* Q, const void* K, const void* Vt, void* O, float* L,
+                             float* S, void* P, float c, int T, int Hq, int Hkv, void* stream) {
+  const int st = sattn_mat_fwd_check(Q, K, Vt, O, L, S, P, c, T, Hq, Hkv);
+  if (st != SATTN_OK) return st;
+  const int dst = check_device();
+  if (dst != SATTN_OK) return dst;
+  const hipStream_t strm = static_cast<hipStream_t>(stream);
+  half_t* p = static_cast<half_t*>(P);
+  launch_scores(static_cast<const half_t*>(Q), static_cast<const half_t*>(K), S, c, T, Hq, Hkv,
+                strm);
+  launch_softmax(S, p, L, T, Hq, strm);
+  launch_pv(p, static_cast<const half_t*>(Vt), static_cast<half_t*>(O), T, Hq, Hkv, strm);
+  return launched();
+}
+
+extern "C" int sattn_mat_scores(const void* Q, const void* K, float* S, float c, int T, int Hq,
+                                int Hkv, void* stream) {
+  const int st = sattn_mat_scores_check(Q, K, S, c, T, Hq, Hkv);
+  if (st != SATTN_OK) return st;
+  const int dst = check_device();
+  if (dst != SATTN_OK) return dst;
+  launch_scores(static_cast<const half_t*>(Q), static_cast<const half_t*>(K), S, c, T, Hq, Hkv,
+                static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+extern "C" int sattn_mat_softmax(const float* S, void* P, float* L, int T, int Hq,
+                                 void* stream) {
+  const int st = sattn_mat_softmax_check(S, P, L, T, Hq);
+  if (st != SATTN_OK) return st;
+  const int dst = check_device();
+  if (dst != SATTN_OK) return dst;
+  launch_softmax(S, static_cast<half_t*>(P), L, T, Hq, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+extern "C" int sattn_mat_pv(const void* P, const void* Vt, void* O, int T, int Hq, int Hkv,
+                            void* stream) {
+  const int st = sattn_mat_pv_check(P, Vt, O, T, Hq, Hkv);
+  if (st != SATTN_OK) return st;
+  const int dst = check_device();
+  if (dst != SATTN_OK) return dst;
+  launch_pv(static_cast<const half_t*>(P), static_cast<const half_t*>(Vt), static_cast<half_t*>(O),
+            T, Hq, Hkv, static_cast<hipStream_t>(stream));
+  return launched();
+}

@@ -53,6 +53,22 @@ _lib.sattn_fwd_check.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void
 _lib.sattn_status_string.restype = ctypes.c_char_p
 _lib.sattn_status_string.argtypes = [ctypes.c_int]
 _P, _F, _I, _U64 = ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_ulonglong
+_lib.sattn_mat_fwd.restype = ctypes.c_int
+_lib.sattn_mat_fwd.argtypes = [_P] * 7 + [_F, _I, _I, _I, _P]
+_lib.sattn_mat_scores.restype = ctypes.c_int
+_lib.sattn_mat_scores.argtypes = [_P] * 3 + [_F, _I, _I, _I, _P]
+_lib.sattn_mat_softmax.restype = ctypes.c_int
+_lib.sattn_mat_softmax.argtypes = [_P] * 3 + [_I, _I, _P]
+_lib.sattn_mat_pv.restype = ctypes.c_int
+_lib.sattn_mat_pv.argtypes = [_P] * 3 + [_I, _I, _I, _P]
+_lib.sattn_mat_scores_check.restype = ctypes.c_int
+_lib.sattn_mat_scores_check.argtypes = [_P] * 3 + [_F, _I, _I, _I]
+_lib.sattn_mat_softmax_check.restype = ctypes.c_int
+_lib.sattn_mat_softmax_check.argtypes = [_P] * 3 + [_I, _I]
+_lib.sattn_mat_pv_check.restype = ctypes.c_int
+_lib.sattn_mat_pv_check.argtypes = [_P] * 3 + [_I, _I, _I]
+_lib.sattn_mat_fwd_check.restype = ctypes.c_int
+_lib.sattn_mat_fwd_check.argtypes = [_P] * 7 + [_F, _I, _I, _I]
 _lib.sattn_bwd_query.restype = ctypes.c_int
 _lib.sattn_bwd_query.argtypes = [_P] * 8 + [_F, _F, _I, _I, _I, _P]
 _lib.sattn_bwd_key.restype = ctypes.c_int
@@ -81,7 +97,9 @@ HEAD_DIM = 64
 
 EXPORTS = ("sattn_fwd", "sattn_fwd_vrows", "sattn_fwd_check", "sattn_status_string", "sattn_bwd_query",
            "sattn_bwd_key", "sattn_bwd", "sattn_bwd_workspace_bytes", "sattn_bwd_check",
-           "sattn_bwd_query_check", "sattn_bwd_key_check")
+           "sattn_bwd_query_check", "sattn_bwd_key_check", "sattn_mat_fwd",
+           "sattn_mat_fwd_check", "sattn_mat_scores", "sattn_mat_softmax", "sattn_mat_pv",
+           "sattn_mat_scores_check", "sattn_mat_softmax_check", "sattn_mat_pv_check")
 
 
 class SattnError(RuntimeError):
@@ -273,3 +291,71 @@ def bwd(q, k, vt, o, do, lse, c, s, dq=None, dk=None, dvt=None, D=None, workspac
     if st != SATTN_OK:
         raise SattnError(st)
     return dq, dk, dvt, D
+
+
+# --------------------------------------------------------------------------
+# materialised path
+# --------------------------------------------------------------------------
+def sattn_mat_fwd(Q, K, Vt, O, L, S, P, c, T, Hq, Hkv, stream=None) -> int:
+    """The C entry point with raw device addresses; returns the status code."""
+    return _lib.sattn_mat_fwd(Q, K, Vt, O, L, S, P, ctypes.c_float(c), T, Hq, Hkv, stream)
+
+
+def sattn_mat_scores(Q, K, S, c, T, Hq, Hkv, stream=None) -> int:
+    return _lib.sattn_mat_scores(Q, K, S, ctypes.c_float(c), T, Hq, Hkv, stream)
+
+
+def sattn_mat_softmax(S, P, L, T, Hq, stream=None) -> int:
+    return _lib.sattn_mat_softmax(S, P, L, T, Hq, stream)
+
+
+def sattn_mat_pv(P, Vt, O, T, Hq, Hkv, stream=None) -> int:
+    return _lib.sattn_mat_pv(P, Vt, O, T, Hq, Hkv, stream)
+
+
+def sattn_mat_scores_check(Q, K, S, c, T, Hq, Hkv) -> int:
+    return _lib.sattn_mat_scores_check(Q, K, S, ctypes.c_float(c), T, Hq, Hkv)
+
+
+def sattn_mat_softmax_check(S, P, L, T, Hq) -> int:
+    return _lib.sattn_mat_softmax_check(S, P, L, T, Hq)
+
+
+def sattn_mat_pv_check(P, Vt, O, T, Hq, Hkv) -> int:
+    return _lib.sattn_mat_pv_check(P, Vt, O, T, Hq, Hkv)
+
+
+def sattn_mat_fwd_check(Q, K, Vt, O, L, S, P, c, T, Hq, Hkv) -> int:
+    return _lib.sattn_mat_fwd_check(Q, K, Vt, O, L, S, P, ctypes.c_float(c), T, Hq, Hkv)
+
+
+def mat_fwd(q, k, vt, c, scores=None, probs=None, out=None, lse=None, stream=None):
+    """The materialised path on torch GPU tensors (layouts as ``fwd``).
+
+    Returns ``(O, L, S, P)``: float16 [T][Hq*64], float32 [Hq][T], and the
+    planes float32 / float16 [Hq][T][T] (entries above the diagonal are left
+    as allocated).
+    """
+    import torch
+    Hq, T, D = q.shape
+    Hkv = k.shape[0]
+    if D != HEAD_DIM or tuple(k.shape) != (Hkv, T, D) or tuple(vt.shape) != (Hkv, D, T):
+        raise ValueError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} vt{tuple(vt.shape)}")
+    dev = q.device
+    if scores is None:
+        scores = torch.empty((Hq, T, T), dtype=torch.float32, device=dev)
+    if probs is None:
+        probs = torch.empty((Hq, T, T), dtype=torch.float16, device=dev)
+    if out is None:
+        out = torch.empty((T, Hq * D), dtype=torch.float16, device=dev)
+    if lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = sattn_mat_fwd(q.data_ptr(), k.data_ptr(), vt.data_ptr(), out.data_ptr(),
+                           lse.data_ptr(), scores.data_ptr(), probs.data_ptr(), float(c), T, Hq,
+                           Hkv, stream.cuda_stream)
+    if st != SATTN_OK:
+        raise SattnError(st)
+    return out, lse, scores, probs

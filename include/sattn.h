@@ -198,6 +198,49 @@ int sattn_bwd_key_check(const void* Q, const void* K, const void* Vt, const void
                         const void* workspace, unsigned long long workspace_bytes, float c,
                         float s, int T, int Hq, int Hkv);
 
+/*
+ * sattn_mat_fwd: the materialised causal attention, the baseline the
+ * streaming forward avoids (the pages' materialised path: the Graph page's
+ * scores plane cgScores, 4*H*T^2 bytes, and its binary16 variant; the causal
+ * softmax device image; probabilities rounded to binary16 before their
+ * product with V).  Three launches on `stream`:
+ *   S[h][i][j] = c (q_i . k_j)                  binary32, base-2 units
+ *   L[h][i]    = log2 sum_{j<=i} 2^S[h][i][j]   binary32
+ *   P[h][i][j] = 2^(S[h][i][j] - L[h][i])       rounded to binary16
+ *   O[i][h*64+d] = sum_{j<=i} P[h][i][j] V_j[d] binary32 sums, binary16 result
+ * for keys j <= i.
+ *   Q, K, Vt, O, L  as for sattn_fwd (O and L: every element written)
+ *   S   device, binary32 [Hq][T][T]: elements with j <= i are written, the
+ *       others are neither written nor used
+ *   P   device, binary16 [Hq][T][T]: likewise
+ * S and P are caller-owned planes (16-byte aligned) that may not overlap
+ * anything else; Hq * T * T * 4 must not exceed 2^40.  Validation as
+ * sattn_fwd plus those planes; asynchronous like sattn_fwd.
+ */
+int sattn_mat_fwd(const void* Q, const void* K, const void* Vt, void* O, float* L, float* S,
+                  void* P, float c, int T, int Hq, int Hkv, void* stream);
+
+/* sattn_mat_fwd_check: the validation of sattn_mat_fwd alone (no HIP call). */
+int sattn_mat_fwd_check(const void* Q, const void* K, const void* Vt, const void* O,
+                        const float* L, const float* S, const void* P, float c, int T, int Hq,
+                        int Hkv);
+
+/*
+ * The three launches of sattn_mat_fwd, one at a time (enqueue them in this
+ * order on one stream): sattn_mat_scores writes S; sattn_mat_softmax reads S
+ * and writes P and L; sattn_mat_pv reads P and V^T and writes O.  Arguments
+ * and layouts as for sattn_mat_fwd; each validates its own (the *_check
+ * functions, no HIP call) before enqueueing anything.
+ */
+int sattn_mat_scores(const void* Q, const void* K, float* S, float c, int T, int Hq, int Hkv,
+                     void* stream);
+int sattn_mat_softmax(const float* S, void* P, float* L, int T, int Hq, void* stream);
+int sattn_mat_pv(const void* P, const void* Vt, void* O, int T, int Hq, int Hkv, void* stream);
+int sattn_mat_scores_check(const void* Q, const void* K, const float* S, float c, int T, int Hq,
+                           int Hkv);
+int sattn_mat_softmax_check(const float* S, const void* P, const float* L, int T, int Hq);
+int sattn_mat_pv_check(const void* P, const void* Vt, const void* O, int T, int Hq, int Hkv);
+
 /* sattn_status_string: a static, NUL-terminated description of a status code
  * (an unknown code gives "unknown sattn status").  Never NULL. */
 const char* sattn_status_string(int status);

@@ -33,7 +33,9 @@ def test_header_declares_the_entry_points():
         "sattn_fwd", "sattn_fwd_vrows", "sattn_fwd_check", "sattn_status_string", "sattn_bwd",
         "sattn_bwd_check",
         "sattn_bwd_key", "sattn_bwd_key_check", "sattn_bwd_query", "sattn_bwd_query_check",
-        "sattn_bwd_workspace_bytes"])
+        "sattn_bwd_workspace_bytes", "sattn_mat_fwd", "sattn_mat_fwd_check",
+        "sattn_mat_scores", "sattn_mat_softmax", "sattn_mat_pv", "sattn_mat_scores_check",
+        "sattn_mat_softmax_check", "sattn_mat_pv_check"])
 
 
 def test_library_exports_every_declared_symbol(sattn):
