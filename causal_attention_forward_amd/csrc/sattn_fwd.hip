@@ -53,6 +53,9 @@
 //  * Workgroups are dealt to the eight XCDs round-robin; they are renumbered
 //    so that each XCD receives a contiguous run ordered K/V head first,
 //    keeping one K/V head's tiles in one XCD's L2.
+//  * Problems with too few query blocks for eight-wave workgroups on every CU
+//    go to the split-key kernel of sattn_fwd_split.hip, which walks each
+//    block's key range with four waves at once.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -62,6 +65,7 @@
 #include <type_traits>
 
 #include "sattn.h"
+#include "sattn_internal.h"
 
 namespace {
 
@@ -623,19 +627,14 @@ void launch(const half_t* Q, const half_t* K, const half_t* Vt, half_t* O, float
                      nHeadGroups);
 }
 
-// Eight-wave workgroups (one per CU) feed each K/V tile to twice the query
-// rows; when they would leave CUs idle, four-wave workgroups (two per CU)
-// double the number of workgroups.
+// Eight-wave workgroups (one per CU); problems too small to give every CU
+// one go to the split-key kernel instead (see forward()).  The kernel also
+// builds for four-wave workgroups (two per CU), which measured slower than
+// the split-key kernel wherever eight-wave ones cannot fill the chip.
 template <int GW, bool VT_VEC, bool VROWS>
 void launch_nw(const half_t* Q, const half_t* K, const half_t* Vt, half_t* O, float* L, float c,
                int T, int Hq, int Hkv, hipStream_t stream) {
-  const int nPairs = ((T + 31) / 32 + 1) / 2;
-  const long long grid8 =
-      (long long)((nPairs + 8 / GW - 1) / (8 / GW)) * Hkv * ((Hq / Hkv) / GW);
-  if (grid8 >= kCus)
-    launch<8, GW, VT_VEC, VROWS>(Q, K, Vt, O, L, c, T, Hq, Hkv, stream);
-  else
-    launch<4, GW, VT_VEC, VROWS>(Q, K, Vt, O, L, c, T, Hq, Hkv, stream);
+  launch<8, GW, VT_VEC, VROWS>(Q, K, Vt, O, L, c, T, Hq, Hkv, stream);
 }
 
 // V^T chunks of 8 keys are whole 16-byte loads only when T % 8 == 0; V rows
@@ -664,6 +663,15 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* L, floa
   half_t* o = static_cast<half_t*>(O);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int G = Hq / Hkv;
+  const int GW = G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
+  const int nPairs = ((T + 31) / 32 + 1) / 2;
+  const long long grid8 = (long long)((nPairs + 8 / GW - 1) / (8 / GW)) * Hkv * (G / GW);
+  if (grid8 < kCus) {
+    // too few query blocks to fill the chip with eight-wave workgroups: split
+    // each block's key range over the four waves of a workgroup instead
+    sattn_fwd_split_launch(Q, K, V, O, L, c, T, Hq, Hkv, VROWS, s);
+    return hipGetLastError() == hipSuccess ? SATTN_OK : SATTN_ERR_LAUNCH;
+  }
   if (G % 4 == 0)
     launch_gw<4, VROWS>(q, k, v, o, L, c, T, Hq, Hkv, s);
   else if (G % 2 == 0)
