@@ -203,6 +203,9 @@ sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
   }
   const float Drow = dpart + xlane(dpart, (lane ^ 32) << 2);
   const float negL = live ? -L[(size_t)h * T + row] : 0.0f;
+  float16v negD;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negD[i] = -Drow;
   if (live && g == 0) D[(size_t)h * T + row] = Drow;
 
   // Staging: thread t owns 16-byte chunks t and t + 256 of a K tile (row
@@ -278,8 +281,9 @@ sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
         const half_t* vk = vb + 16 * kk * kRowHalfs;
         const half8 v0 = tr8(vk, vtOff[0][0], vtOff[0][1]);
         const half8 v1 = tr8(vk, vtOff[1][0], vtOff[1][1]);
-        p0 = mfma(v0, dof[kk], kk == 0 ? float16v{} : p0);
-        p1 = mfma(v1, dof[kk], kk == 0 ? float16v{} : p1);
+        // the dP^T accumulators start at -D, so they end as dP^T - D
+        p0 = mfma(v0, dof[kk], kk == 0 ? negD : p0);
+        p1 = mfma(v1, dof[kk], kk == 0 ? negD : p1);
       }
       // the diagonal: key 64kt + 16(i/8) + 8g + i%8 (+32) is kept iff <= row
       if (kt * kTile + kTile - 1 > waveRow0) {
@@ -294,8 +298,8 @@ sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
       // P^T = 2^(S^T c - L), dS^T = P^T (dP^T - D)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c, negL)) * (p0[i] - Drow);
-        s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c, negL)) * (p1[i] - Drow);
+        s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c, negL)) * p0[i];
+        s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c, negL)) * p1[i];
       }
       const half8 ds[4] = {pack8(s0, 0), pack8(s0, 1), pack8(s1, 0), pack8(s1, 1)};
       // dQ^T += K^T dS^T: d = n (dq0) and 32 + n (dq1), keys 16ck + 8g .. +7
@@ -376,7 +380,7 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
 
   // Staging: thread t owns 16-byte chunks t and t + 256 of the Q tile and of
   // the dO tile (row c/8, column chunk c%8); threads 0..63 the tile's L and
-  // threads 64..127 its D (rows past T read L = +inf and D = 0, so P = 0).
+  // threads 64..127 its -D (rows past T read L = +inf and -D = 0, so P = 0).
   const int cr = tid >> 3, cc = tid & 7;
   const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<half_t*>(Q + (size_t)h * T * kD), 0, T * kD * 2, kBufferWord3);
@@ -396,7 +400,7 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
     if (tid < 2 * kTile) {
       const int q = q0 + (tid & (kTile - 1));
       const bool isL = tid < kTile;
-      rst = q < T ? (isL ? L : D)[(size_t)h * T + q] : (isL ? INFINITY : 0.0f);
+      rst = q < T ? (isL ? L[(size_t)h * T + q] : -D[(size_t)h * T + q]) : (isL ? INFINITY : 0.0f);
     }
   };
   auto store = [&](int buf) {
@@ -430,6 +434,22 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
     if (it * kTile + kTile - 1 >= waveKey0) {
       const half_t* qb = qbuf + buf * kTileHalfs;
       const half_t* ob = obuf + buf * kTileHalfs;
+      // -D of element i's query 16(i/8) + 8g + i%8 (+32 for x1): the dP
+      // accumulators start there, so they end as dP - D
+      const float* lt = rowterms[buf][0];
+      const float* dt = rowterms[buf][1];
+      float16v nd0, nd1;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float4v d0 = *reinterpret_cast<const float4v*>(dt + 16 * b + 8 * g);
+        const float4v d1 = *reinterpret_cast<const float4v*>(dt + 16 * b + 8 * g + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float16v& nd = b < 2 ? nd0 : nd1;
+          nd[8 * (b & 1) + e] = d0[e];
+          nd[8 * (b & 1) + 4 + e] = d1[e];
+        }
+      }
       // S = Q K^T and dP = dO V^T: queries 0..31 (x0) and 32..63 (x1) of the tile
       float16v s0, s1, p0, p1;
 #pragma unroll
@@ -440,8 +460,8 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
         s1 = mfma(a1, kf[kk], kk == 0 ? float16v{} : s1);
         const half8 b0 = ld8(ob + nOff[kk]);
         const half8 b1 = ld8(ob + nOff[kk] + 32 * kRowHalfs);
-        p0 = mfma(b0, vf[kk], kk == 0 ? float16v{} : p0);
-        p1 = mfma(b1, vf[kk], kk == 0 ? float16v{} : p1);
+        p0 = mfma(b0, vf[kk], kk == 0 ? nd0 : p0);
+        p1 = mfma(b1, vf[kk], kk == 0 ? nd1 : p1);
       }
       // the diagonal: query 64it + 16(i/8) + 8g + i%8 (+32) is kept iff >= key
       if (it * kTile < waveKey0 + 31) {
@@ -455,26 +475,21 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
       }
       // P = 2^(S c - L) and dS = P (dP - D), eight queries at a time: block
       // b holds queries 16b + 8g .. +7 of the tile (elements 8(b%2) .. of x(b/2))
-      const float* lt = rowterms[buf][0];
-      const float* dt = rowterms[buf][1];
       half8 pb[4], db[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int q = 16 * b + 8 * g;
         const float4v l0 = *reinterpret_cast<const float4v*>(lt + q);
         const float4v l1 = *reinterpret_cast<const float4v*>(lt + q + 4);
-        const float4v d0 = *reinterpret_cast<const float4v*>(dt + q);
-        const float4v d1 = *reinterpret_cast<const float4v*>(dt + q + 4);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int i = 8 * (b & 1) + e;
           const float sv = b < 2 ? s0[i] : s1[i];
           const float pv = b < 2 ? p0[i] : p1[i];
           const float lv = e < 4 ? l0[e] : l1[e - 4];
-          const float dv = e < 4 ? d0[e] : d1[e - 4];
           const float P = __builtin_amdgcn_exp2f(fmaf(sv, c, -lv));
           pb[b][e] = (half_t)P;
-          db[b][e] = (half_t)(P * (pv - dv));
+          db[b][e] = (half_t)(P * pv);
         }
       }
       // dV^T += dO^T P and dK^T += Q^T dS: d = n (x0) and 32 + n (x1),
