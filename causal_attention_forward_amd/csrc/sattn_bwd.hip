@@ -97,6 +97,12 @@ __device__ __forceinline__ int krow(int m) {
 
 __device__ __forceinline__ half8 ld8(const half_t* p) { return *reinterpret_cast<const half8*>(p); }
 
+// Workgroup barrier without __syncthreads()'s wait for every outstanding
+// load: callers wait for their LDS stores (kLdsDone) and let the global loads
+// of later tiles stay in flight across it.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+constexpr int kLdsDone = 0xC07F;  // s_waitcnt lgkmcnt(0), other counters unconstrained
+
 // ds_read_b64_tr_b16 at p: within each 16-lane group, lane 4a + b supplies
 // the address of row a, columns 4b'..4b'+3 of a block, and lane t receives
 // rows 0..3 of the column that lanes 4(t/4)'s supplier pointed at, offset t%4.
@@ -216,16 +222,20 @@ sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
   const half_t* Vh = Vt + (size_t)kv * kD * T;
   const __amdgpu_buffer_rsrc_t vrsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(Vh), 0, kD * T * 2, kBufferWord3);
-  int4v kst[2], vst[2];
-  auto load = [&](int kt) {
+  // Two register sets by tile parity: tile kt + 2 is loaded at step kt and
+  // stored at step kt + 1, so its loads have a whole step to arrive.  Tiles
+  // past the end read as zeros (range checks), so every step issues the same
+  // loads and stores and the compiler's load waits stay exact.
+  int4v kst[2][2], vst[2][2];  // [set][chunk]
+  auto load = [&](int kt, int set) {
     const int key0 = kt * kTile;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int r = cr + 32 * p;
-      kst[p] = __builtin_amdgcn_raw_buffer_load_b128(krsrc, ((key0 + r) * kD + cc * 8) * 2, 0, 0);
+      kst[set][p] = __builtin_amdgcn_raw_buffer_load_b128(krsrc, ((key0 + r) * kD + cc * 8) * 2, 0, 0);
       if (VT_VEC) {
         const int off = key0 + cc * 8 < T ? (r * T + key0 + cc * 8) * 2 : kOutOfRange;
-        vst[p] = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off, 0, 0);
+        vst[set][p] = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off, 0, 0);
       } else {
         half8 v;
 #pragma unroll
@@ -233,16 +243,16 @@ sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
           const int key = key0 + cc * 8 + e;
           v[e] = key < T ? Vh[(size_t)r * T + key] : (half_t)0;
         }
-        vst[p] = __builtin_bit_cast(int4v, v);
+        vst[set][p] = __builtin_bit_cast(int4v, v);
       }
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, int set) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int off = buf * kTileHalfs + chunk_offset(cr + 32 * p, cc);
-      *reinterpret_cast<int4v*>(kbuf + off) = kst[p];
-      *reinterpret_cast<int4v*>(vbuf + off) = vst[p];
+      *reinterpret_cast<int4v*>(kbuf + off) = kst[set][p];
+      *reinterpret_cast<int4v*>(vbuf + off) = vst[set][p];
     }
   };
 
@@ -261,12 +271,13 @@ sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
     }
 
   float16v dq0 = {}, dq1 = {};
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) load(kt + 1);
+  load(0, 0);
+  load(1, 1);
+  store(0, 0);
+  __builtin_amdgcn_s_waitcnt(kLdsDone);
+  barrier();
+  auto tile_step = [&](int kt, int buf) {
+    load(kt + 2, buf);
     if (kt * kTile <= waveLast) {
       const half_t* kb = kbuf + buf * kTileHalfs;
       const half_t* vb = vbuf + buf * kTileHalfs;
@@ -312,8 +323,13 @@ sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
         dq1 = mfma(k1, ds[ck], dq1);
       }
     }
-    if (kt + 1 < nkt) store(buf ^ 1);
-    __syncthreads();
+    store(buf ^ 1, buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(kLdsDone);
+    barrier();
+  };
+  for (int kt = 0; kt < nkt; kt += 2) {  // unrolled by two: the sets are fixed registers
+    tile_step(kt, 0);
+    if (kt + 1 < nkt) tile_step(kt + 1, 1);
   }
 
   // dQ = s * sum: accumulator element 4q + e of lane (n, g) is d = 8q + 4g + e
@@ -386,31 +402,34 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
       const_cast<half_t*>(Q + (size_t)h * T * kD), 0, T * kD * 2, kBufferWord3);
   const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<half_t*>(dO + (size_t)h * kD), 0, (T * Hq - h) * kD * 2, kBufferWord3);
-  int4v qst[2], ost[2];
-  float rst = 0.0f;
-  auto load = [&](int it) {
+  // Two register sets by tile parity, loads two tiles ahead (as in the query
+  // launch); tiles past the end read as zeros and their row terms as L = +inf,
+  // -D = 0.
+  int4v qst[2][2], ost[2][2];  // [set][chunk]
+  float rst[2] = {0.0f, 0.0f};
+  auto load = [&](int it, int set) {
     const int q0 = it * kTile;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int r = q0 + cr + 32 * p;
-      qst[p] = __builtin_amdgcn_raw_buffer_load_b128(qrsrc, (r * kD + cc * 8) * 2, 0, 0);
-      ost[p] = __builtin_amdgcn_raw_buffer_load_b128(
+      qst[set][p] = __builtin_amdgcn_raw_buffer_load_b128(qrsrc, (r * kD + cc * 8) * 2, 0, 0);
+      ost[set][p] = __builtin_amdgcn_raw_buffer_load_b128(
           orsrc, (int)(((unsigned)r * (unsigned)Hq * kD + cc * 8) * 2u), 0, 0);
     }
     if (tid < 2 * kTile) {
       const int q = q0 + (tid & (kTile - 1));
       const bool isL = tid < kTile;
-      rst = q < T ? (isL ? L[(size_t)h * T + q] : -D[(size_t)h * T + q]) : (isL ? INFINITY : 0.0f);
+      rst[set] = q < T ? (isL ? L[(size_t)h * T + q] : -D[(size_t)h * T + q]) : (isL ? INFINITY : 0.0f);
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, int set) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int off = buf * kTileHalfs + chunk_offset(cr + 32 * p, cc);
-      *reinterpret_cast<int4v*>(qbuf + off) = qst[p];
-      *reinterpret_cast<int4v*>(obuf + off) = ost[p];
+      *reinterpret_cast<int4v*>(qbuf + off) = qst[set][p];
+      *reinterpret_cast<int4v*>(obuf + off) = ost[set][p];
     }
-    if (tid < 2 * kTile) rowterms[buf][tid >> 6][tid & (kTile - 1)] = rst;
+    if (tid < 2 * kTile) rowterms[buf][tid >> 6][tid & (kTile - 1)] = rst[set];
   };
 
   // natural Q / dO rows (queries krow(n), d = 16kk + 8g ..)
@@ -425,12 +444,13 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
     for (int hi = 0; hi < 2; ++hi) tOff[mh][hi] = tr_offset(lane, false, mh, hi);
 
   float16v dk0 = {}, dk1 = {}, dv0 = {}, dv1 = {};
-  load(ft);
-  store(0);
-  __syncthreads();
-  for (int it = ft; it < nt; ++it) {
-    const int buf = (it - ft) & 1;
-    if (it + 1 < nt) load(it + 1);
+  load(ft, 0);
+  load(ft + 1, 1);
+  store(0, 0);
+  __builtin_amdgcn_s_waitcnt(kLdsDone);
+  barrier();
+  auto tile_step = [&](int it, int buf) {
+    load(it + 2, buf);
     if (it * kTile + kTile - 1 >= waveKey0) {
       const half_t* qb = qbuf + buf * kTileHalfs;
       const half_t* ob = obuf + buf * kTileHalfs;
@@ -508,8 +528,13 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
         dk1 = mfma(q1, db[ck], dk1);
       }
     }
-    if (it + 1 < nt) store(buf ^ 1);
-    __syncthreads();
+    store(buf ^ 1, buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(kLdsDone);
+    barrier();
+  };
+  for (int it = ft; it < nt; it += 2) {  // unrolled by two: the sets are fixed registers
+    tile_step(it, 0);
+    if (it + 1 < nt) tile_step(it + 1, 1);
   }
 
   // accumulator element 4q + e of lane (n, g) is d = 8q + 4g + e of key n
