@@ -176,7 +176,8 @@ def bench_backward(args, torch, sattn, x, w):
     query_flops = 1.5 * causal_flops(T, Hq)    # S, dP, dQ
     key_tf = key_flops / (key_ms * 1e-3) / 1e12
     out = {
-        "metric": "causal attn bwd TFLOP/s (S, dP, dQ, dK, dV = 2.5x fwd flop), T=4096 Hq=32 Hkv=8 d=64",
+        "metric": "causal attn bwd TFLOP/s (S, dP, dQ, dK, dV = 2.5x fwd flop), "
+                  f"T={T} Hq={Hq} Hkv={Hkv} d=64",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -356,6 +357,67 @@ def sweep(torch, sattn, workloads, make_workload, reps=5, calls=50):
         torch.cuda.empty_cache()
 
 
+def sweep_backward(torch, sattn, workloads, make_workload, reps=5, calls=20):
+    """The backward on every synthetic workload (O and L from the forward on
+    the same inputs, dO seeded): median over `reps` runs of `calls` launches,
+    input sets rotated as in `sweep`."""
+    import math
+    import statistics
+    from causal_attention_forward_amd.inputs import make_output_gradient
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    for idx, w in enumerate(workloads):
+        x = make_workload(idx)
+        T, Hq, Hkv = x.T, x.Hq, x.Hkv
+        dO = make_output_gradient(T, Hq, idx)
+        # read Q, K, V^T, O, dO (binary16), L; write dQ, dK, dV^T, D (binary32)
+        nbytes = 2 * 64 * T * (3 * Hq + 2 * Hkv) + 4 * T * Hq + 4 * 64 * T * (Hq + 2 * Hkv) + 4 * T * Hq
+        nsets = min(32, max(2, math.ceil(300e6 / nbytes)))
+        need = sattn.sattn_bwd_workspace_bytes(T, Hq, Hkv)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        sets = []
+        for _ in range(nsets):
+            q, k, vt = (torch.from_numpy(a).to(dev) for a in (x.Q, x.K, x.Vt))
+            O, L = sattn.fwd(q, k, vt, x.c)
+            f32 = dict(dtype=torch.float32, device=dev)
+            sets.append((q, k, vt, O, torch.from_numpy(dO).to(dev), L,
+                         torch.empty((Hq, T, 64), **f32), torch.empty((Hkv, T, 64), **f32),
+                         torch.empty((Hkv, 64, T), **f32), torch.empty((Hq, T), **f32)))
+
+        def call(i):
+            q, k, vt, O, g, L, dQ, dK, dVt, D = sets[i % nsets]
+            st = sattn.sattn_bwd(q.data_ptr(), k.data_ptr(), vt.data_ptr(), O.data_ptr(),
+                                 g.data_ptr(), L.data_ptr(), dQ.data_ptr(), dK.data_ptr(),
+                                 dVt.data_ptr(), D.data_ptr(), ws.data_ptr(), need, x.c, 0.125,
+                                 T, Hq, Hkv, sp)
+            assert st == sattn.SATTN_OK, st
+
+        for i in range(max(40, 2 * nsets)):
+            call(i)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for i in range(calls):
+                call(i)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            times.append(ev0.elapsed_time(ev1) / calls)
+        ms = statistics.median(times)
+        tflops = backward_flops(T, Hq) / (ms * 1e-3) / 1e12
+        print(json.dumps({
+            "sweep_backward": w.name, "T": T, "Hq": Hq, "Hkv": Hkv,
+            "us_per_call": round(ms * 1e3, 2), "tflops_algorithmic": round(tflops, 2),
+            "pct_fp16_peak": round(100 * tflops / PEAK_FP16_TFLOPS, 2),
+            "compulsory_bytes": nbytes, "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "input_sets": nsets}), flush=True)
+        del sets, ws
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -401,7 +463,10 @@ def main():
     from causal_attention_forward_amd.inputs import WORKLOADS, make_workload
 
     if args.sweep:
-        sweep(torch, sattn, WORKLOADS, make_workload)
+        if args.backward:
+            sweep_backward(torch, sattn, WORKLOADS, make_workload)
+        else:
+            sweep(torch, sattn, WORKLOADS, make_workload)
         return
 
     w = WORKLOADS[args.workload]
@@ -470,10 +535,12 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
-    traffic = None if args.vrows else measured_traffic()
+    # the counter summary covers the default workload only
+    traffic = None if args.vrows or args.workload != WORKLOAD_INDEX else measured_traffic()
+    shape = f"T={x.T} Hq={x.Hq} Hkv={x.Hkv} d=64"
     out = {
-        "metric": ("causal attn fwd (V as rows) TFLOP/s, T=4096 Hq=32 Hkv=8 d=64" if args.vrows else
-                   "causal attn fwd TFLOP/s and % fp16 MFMA peak, T=4096 Hq=32 Hkv=8 d=64"),
+        "metric": (f"causal attn fwd (V as rows) TFLOP/s, {shape}" if args.vrows else
+                   f"causal attn fwd TFLOP/s and % fp16 MFMA peak, {shape}"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

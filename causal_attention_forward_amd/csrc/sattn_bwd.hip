@@ -34,9 +34,11 @@
 //    of anything is written to memory.
 //  * A wave owns 32 queries (query launch) or 32 keys (key launch); a
 //    workgroup is four waves on consecutive rows and stages each 64-row tile
-//    once for all of them, double-buffered.  Each XCD receives a contiguous
+//    once for all of them, loaded two tiles ahead.  A workgroup takes a heavy
+//    block and then its light partner (blocks b and n-1-b), so every
+//    workgroup carries the same causal work; each XCD receives a contiguous
 //    run of workgroups ordered K/V head first (that head's tiles stay in its
-//    L2), then heaviest first.
+//    L2).
 //  * With GQA the key launch writes one dK and one dV^T plane per query head
 //    into a caller-provided workspace and a reduction sums the G planes of
 //    each K/V head in head order; with Hq == Hkv it writes dK and dV^T
@@ -161,13 +163,13 @@ __device__ __forceinline__ half8 pack8(const float16v& x, int h) {
 // -------------------------------------------------------------------------
 // Query launch: D and dQ.  Workgroup = kNW waves x 32 query rows of head h.
 // -------------------------------------------------------------------------
-template <bool VT_VEC>
+template <bool VT_VEC, bool PAIRED>
 __global__ void __launch_bounds__(64 * kNW, 2)
 sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
                   const half_t* __restrict__ Vt, const half_t* __restrict__ O,
                   const half_t* __restrict__ dO, const float* __restrict__ L,
                   float* __restrict__ dQ, float* __restrict__ D, float c, float s, int T, int Hq,
-                  int G, int nBlocks) {
+                  int G, int nBlocks, int nPairs) {
   __shared__ __attribute__((aligned(16))) half_t smem[4 * kTileHalfs];
   half_t* const kbuf = smem;                   // K tiles [2][64 keys][72]
   half_t* const vbuf = smem + 2 * kTileHalfs;  // V^T tiles [2][64 d][72]
@@ -178,184 +180,190 @@ sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
   const int n = lane & 31;
   const int g = lane >> 5;
 
-  // K/V head first, then query blocks heaviest first, then the group's heads
+  // K/V head first, then query blocks heaviest first (paired: heavy block
+  // nBlocks-1-p, then light block p, so every workgroup carries the same
+  // causal work), then the group's heads
   const int lid = xcd_order();
-  const int kv = lid / (nBlocks * G);
-  const int rem = lid - kv * nBlocks * G;
-  const int blk = nBlocks - 1 - rem / G;
+  const int kv = lid / (nPairs * G);
+  const int rem = lid - kv * nPairs * G;
+  const int pair = rem / G;
   const int h = kv * G + rem % G;
-  const int row0 = blk * 32 * kNW;
-  const int waveRow0 = row0 + 32 * wave;
-  const int row = waveRow0 + n;
-  const bool live = row < T;
-  const int nkt = min(T - 1, row0 + 32 * kNW - 1) / kTile + 1;  // key tiles of the workgroup
-  const int waveLast = min(T - 1, waveRow0 + 31);               // the wave's last row
+  auto run = [&](int blk) {
+    const int row0 = blk * 32 * kNW;
+    const int waveRow0 = row0 + 32 * wave;
+    const int row = waveRow0 + n;
+    const bool live = row < T;
+    const int nkt = min(T - 1, row0 + 32 * kNW - 1) / kTile + 1;  // key tiles of the workgroup
+    const int waveLast = min(T - 1, waveRow0 + 31);               // the wave's last row
 
-  // Q and dO rows as B operands (lane: row n, columns 16kk + 8g .. +7), and D.
-  half8 qf[4], dof[4];
-  float dpart = 0.0f;
-  {
-    const half_t* qrow = Q + ((size_t)h * T + row) * kD + 8 * g;
-    const size_t tok = (size_t)row * Hq * kD + (size_t)h * kD + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const half8 z = {};
-      qf[kk] = live ? ld8(qrow + 16 * kk) : z;
-      dof[kk] = live ? *reinterpret_cast<const half8*>(dO + tok + 16 * kk) : z;
-      const half8 of = live ? *reinterpret_cast<const half8*>(O + tok + 16 * kk) : z;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dpart = fmaf((float)dof[kk][e], (float)of[e], dpart);
-    }
-  }
-  const float Drow = dpart + xlane(dpart, (lane ^ 32) << 2);
-  const float negL = live ? -L[(size_t)h * T + row] : 0.0f;
-  float16v negD;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) negD[i] = -Drow;
-  if (live && g == 0) D[(size_t)h * T + row] = Drow;
-
-  // Staging: thread t owns 16-byte chunks t and t + 256 of a K tile (row
-  // c/8, column chunk c%8) and of a V^T tile.
-  const int cr = tid >> 3, cc = tid & 7;
-  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<half_t*>(K + (size_t)kv * T * kD), 0, T * kD * 2, kBufferWord3);
-  const half_t* Vh = Vt + (size_t)kv * kD * T;
-  const __amdgpu_buffer_rsrc_t vrsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(Vh), 0, kD * T * 2, kBufferWord3);
-  // Two register sets by tile parity: tile kt + 2 is loaded at step kt and
-  // stored at step kt + 1, so its loads have a whole step to arrive.  Tiles
-  // past the end read as zeros (range checks), so every step issues the same
-  // loads and stores and the compiler's load waits stay exact.
-  int4v kst[2][2], vst[2][2];  // [set][chunk]
-  auto load = [&](int kt, int set) {
-    const int key0 = kt * kTile;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int r = cr + 32 * p;
-      kst[set][p] = __builtin_amdgcn_raw_buffer_load_b128(krsrc, ((key0 + r) * kD + cc * 8) * 2, 0, 0);
-      if (VT_VEC) {
-        const int off = key0 + cc * 8 < T ? (r * T + key0 + cc * 8) * 2 : kOutOfRange;
-        vst[set][p] = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off, 0, 0);
-      } else {
-        half8 v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = key0 + cc * 8 + e;
-          v[e] = key < T ? Vh[(size_t)r * T + key] : (half_t)0;
-        }
-        vst[set][p] = __builtin_bit_cast(int4v, v);
-      }
-    }
-  };
-  auto store = [&](int buf, int set) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int off = buf * kTileHalfs + chunk_offset(cr + 32 * p, cc);
-      *reinterpret_cast<int4v*>(kbuf + off) = kst[set][p];
-      *reinterpret_cast<int4v*>(vbuf + off) = vst[set][p];
-    }
-  };
-
-  // natural K rows for S^T (keys krow(n), d = 16kk + 8g ..)
-  int kOff[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) kOff[kk] = chunk_offset(krow(n), 2 * kk + g);
-  // V rows (keys krow(n) + 32 mh) from the V^T tile; K^T rows (d = n + 32 mh) from the K tile
-  int vtOff[2][2], ktOff[2][2];
-#pragma unroll
-  for (int mh = 0; mh < 2; ++mh)
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi) {
-      vtOff[mh][hi] = tr_offset(lane, true, mh, hi);
-      ktOff[mh][hi] = tr_offset(lane, false, mh, hi);
-    }
-
-  float16v dq0 = {}, dq1 = {};
-  load(0, 0);
-  load(1, 1);
-  store(0, 0);
-  __builtin_amdgcn_s_waitcnt(kLdsDone);
-  barrier();
-  auto tile_step = [&](int kt, int buf) {
-    load(kt + 2, buf);
-    if (kt * kTile <= waveLast) {
-      const half_t* kb = kbuf + buf * kTileHalfs;
-      const half_t* vb = vbuf + buf * kTileHalfs;
-      // S^T = K Q^T and dP^T = V dO^T: keys 0..31 (x0) and 32..63 (x1) of the tile
-      float16v s0, s1, p0, p1;
-#pragma unroll
+    // Q and dO rows as B operands (lane: row n, columns 16kk + 8g .. +7), and D.
+    half8 qf[4], dof[4];
+    float dpart = 0.0f;
+    {
+      const half_t* qrow = Q + ((size_t)h * T + row) * kD + 8 * g;
+      const size_t tok = (size_t)row * Hq * kD + (size_t)h * kD + 8 * g;
+  #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const half8 a0 = ld8(kb + kOff[kk]);
-        const half8 a1 = ld8(kb + kOff[kk] + 32 * kRowHalfs);
-        s0 = mfma(a0, qf[kk], kk == 0 ? float16v{} : s0);
-        s1 = mfma(a1, qf[kk], kk == 0 ? float16v{} : s1);
-        const half_t* vk = vb + 16 * kk * kRowHalfs;
-        const half8 v0 = tr8(vk, vtOff[0][0], vtOff[0][1]);
-        const half8 v1 = tr8(vk, vtOff[1][0], vtOff[1][1]);
-        // the dP^T accumulators start at -D, so they end as dP^T - D
-        p0 = mfma(v0, dof[kk], kk == 0 ? negD : p0);
-        p1 = mfma(v1, dof[kk], kk == 0 ? negD : p1);
-      }
-      // the diagonal: key 64kt + 16(i/8) + 8g + i%8 (+32) is kept iff <= row
-      if (kt * kTile + kTile - 1 > waveRow0) {
-        const int lim = row - kt * kTile - 8 * g;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int k = 16 * (i >> 3) + (i & 7);
-          if (k > lim) s0[i] = -INFINITY;
-          if (k + 32 > lim) s1[i] = -INFINITY;
-        }
-      }
-      // P^T = 2^(S^T c - L), dS^T = P^T (dP^T - D)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c, negL)) * p0[i];
-        s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c, negL)) * p1[i];
-      }
-      const half8 ds[4] = {pack8(s0, 0), pack8(s0, 1), pack8(s1, 0), pack8(s1, 1)};
-      // dQ^T += K^T dS^T: d = n (dq0) and 32 + n (dq1), keys 16ck + 8g .. +7
-#pragma unroll
-      for (int ck = 0; ck < 4; ++ck) {
-        const half_t* kc = kb + 16 * ck * kRowHalfs;
-        const half8 k0 = tr8(kc, ktOff[0][0], ktOff[0][1]);
-        const half8 k1 = tr8(kc, ktOff[1][0], ktOff[1][1]);
-        dq0 = mfma(k0, ds[ck], dq0);
-        dq1 = mfma(k1, ds[ck], dq1);
+        const half8 z = {};
+        qf[kk] = live ? ld8(qrow + 16 * kk) : z;
+        dof[kk] = live ? *reinterpret_cast<const half8*>(dO + tok + 16 * kk) : z;
+        const half8 of = live ? *reinterpret_cast<const half8*>(O + tok + 16 * kk) : z;
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) dpart = fmaf((float)dof[kk][e], (float)of[e], dpart);
       }
     }
-    store(buf ^ 1, buf ^ 1);
+    const float Drow = dpart + xlane(dpart, (lane ^ 32) << 2);
+    const float negL = live ? -L[(size_t)h * T + row] : 0.0f;
+    float16v negD;
+  #pragma unroll
+    for (int i = 0; i < 16; ++i) negD[i] = -Drow;
+    if (live && g == 0) D[(size_t)h * T + row] = Drow;
+
+    // Staging: thread t owns 16-byte chunks t and t + 256 of a K tile (row
+    // c/8, column chunk c%8) and of a V^T tile.
+    const int cr = tid >> 3, cc = tid & 7;
+    const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<half_t*>(K + (size_t)kv * T * kD), 0, T * kD * 2, kBufferWord3);
+    const half_t* Vh = Vt + (size_t)kv * kD * T;
+    const __amdgpu_buffer_rsrc_t vrsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(Vh), 0, kD * T * 2, kBufferWord3);
+    // Two register sets by tile parity: tile kt + 2 is loaded at step kt and
+    // stored at step kt + 1, so its loads have a whole step to arrive.  Tiles
+    // past the end read as zeros (range checks), so every step issues the same
+    // loads and stores and the compiler's load waits stay exact.
+    int4v kst[2][2], vst[2][2];  // [set][chunk]
+    auto load = [&](int kt, int set) {
+      const int key0 = kt * kTile;
+  #pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int r = cr + 32 * p;
+        kst[set][p] = __builtin_amdgcn_raw_buffer_load_b128(krsrc, ((key0 + r) * kD + cc * 8) * 2, 0, 0);
+        if (VT_VEC) {
+          const int off = key0 + cc * 8 < T ? (r * T + key0 + cc * 8) * 2 : kOutOfRange;
+          vst[set][p] = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off, 0, 0);
+        } else {
+          half8 v;
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int key = key0 + cc * 8 + e;
+            v[e] = key < T ? Vh[(size_t)r * T + key] : (half_t)0;
+          }
+          vst[set][p] = __builtin_bit_cast(int4v, v);
+        }
+      }
+    };
+    auto store = [&](int buf, int set) {
+  #pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int off = buf * kTileHalfs + chunk_offset(cr + 32 * p, cc);
+        *reinterpret_cast<int4v*>(kbuf + off) = kst[set][p];
+        *reinterpret_cast<int4v*>(vbuf + off) = vst[set][p];
+      }
+    };
+
+    // natural K rows for S^T (keys krow(n), d = 16kk + 8g ..)
+    int kOff[4];
+  #pragma unroll
+    for (int kk = 0; kk < 4; ++kk) kOff[kk] = chunk_offset(krow(n), 2 * kk + g);
+    // V rows (keys krow(n) + 32 mh) from the V^T tile; K^T rows (d = n + 32 mh) from the K tile
+    int vtOff[2][2], ktOff[2][2];
+  #pragma unroll
+    for (int mh = 0; mh < 2; ++mh)
+  #pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        vtOff[mh][hi] = tr_offset(lane, true, mh, hi);
+        ktOff[mh][hi] = tr_offset(lane, false, mh, hi);
+      }
+
+    float16v dq0 = {}, dq1 = {};
+    load(0, 0);
+    load(1, 1);
+    store(0, 0);
     __builtin_amdgcn_s_waitcnt(kLdsDone);
     barrier();
-  };
-  for (int kt = 0; kt < nkt; kt += 2) {  // unrolled by two: the sets are fixed registers
-    tile_step(kt, 0);
-    if (kt + 1 < nkt) tile_step(kt + 1, 1);
-  }
-
-  // dQ = s * sum: accumulator element 4q + e of lane (n, g) is d = 8q + 4g + e
-  if (live) {
-    float* out = dQ + ((size_t)h * T + row) * kD + 4 * g;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4v a = {dq0[4 * q], dq0[4 * q + 1], dq0[4 * q + 2], dq0[4 * q + 3]};
-      const float4v b = {dq1[4 * q], dq1[4 * q + 1], dq1[4 * q + 2], dq1[4 * q + 3]};
-      *reinterpret_cast<float4v*>(out + 8 * q) = a * s;
-      *reinterpret_cast<float4v*>(out + 32 + 8 * q) = b * s;
+    auto tile_step = [&](int kt, int buf) {
+      load(kt + 2, buf);
+      if (kt * kTile <= waveLast) {
+        const half_t* kb = kbuf + buf * kTileHalfs;
+        const half_t* vb = vbuf + buf * kTileHalfs;
+        // S^T = K Q^T and dP^T = V dO^T: keys 0..31 (x0) and 32..63 (x1) of the tile
+        float16v s0, s1, p0, p1;
+  #pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const half8 a0 = ld8(kb + kOff[kk]);
+          const half8 a1 = ld8(kb + kOff[kk] + 32 * kRowHalfs);
+          s0 = mfma(a0, qf[kk], kk == 0 ? float16v{} : s0);
+          s1 = mfma(a1, qf[kk], kk == 0 ? float16v{} : s1);
+          const half_t* vk = vb + 16 * kk * kRowHalfs;
+          const half8 v0 = tr8(vk, vtOff[0][0], vtOff[0][1]);
+          const half8 v1 = tr8(vk, vtOff[1][0], vtOff[1][1]);
+          // the dP^T accumulators start at -D, so they end as dP^T - D
+          p0 = mfma(v0, dof[kk], kk == 0 ? negD : p0);
+          p1 = mfma(v1, dof[kk], kk == 0 ? negD : p1);
+        }
+        // the diagonal: key 64kt + 16(i/8) + 8g + i%8 (+32) is kept iff <= row
+        if (kt * kTile + kTile - 1 > waveRow0) {
+          const int lim = row - kt * kTile - 8 * g;
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int k = 16 * (i >> 3) + (i & 7);
+            if (k > lim) s0[i] = -INFINITY;
+            if (k + 32 > lim) s1[i] = -INFINITY;
+          }
+        }
+        // P^T = 2^(S^T c - L), dS^T = P^T (dP^T - D)
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c, negL)) * p0[i];
+          s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c, negL)) * p1[i];
+        }
+        const half8 ds[4] = {pack8(s0, 0), pack8(s0, 1), pack8(s1, 0), pack8(s1, 1)};
+        // dQ^T += K^T dS^T: d = n (dq0) and 32 + n (dq1), keys 16ck + 8g .. +7
+  #pragma unroll
+        for (int ck = 0; ck < 4; ++ck) {
+          const half_t* kc = kb + 16 * ck * kRowHalfs;
+          const half8 k0 = tr8(kc, ktOff[0][0], ktOff[0][1]);
+          const half8 k1 = tr8(kc, ktOff[1][0], ktOff[1][1]);
+          dq0 = mfma(k0, ds[ck], dq0);
+          dq1 = mfma(k1, ds[ck], dq1);
+        }
+      }
+      store(buf ^ 1, buf ^ 1);
+      __builtin_amdgcn_s_waitcnt(kLdsDone);
+      barrier();
+    };
+    for (int kt = 0; kt < nkt; kt += 2) {  // unrolled by two: the sets are fixed registers
+      tile_step(kt, 0);
+      if (kt + 1 < nkt) tile_step(kt + 1, 1);
     }
-  }
+
+    // dQ = s * sum: accumulator element 4q + e of lane (n, g) is d = 8q + 4g + e
+    if (live) {
+      float* out = dQ + ((size_t)h * T + row) * kD + 4 * g;
+  #pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4v a = {dq0[4 * q], dq0[4 * q + 1], dq0[4 * q + 2], dq0[4 * q + 3]};
+        const float4v b = {dq1[4 * q], dq1[4 * q + 1], dq1[4 * q + 2], dq1[4 * q + 3]};
+        *reinterpret_cast<float4v*>(out + 8 * q) = a * s;
+        *reinterpret_cast<float4v*>(out + 32 + 8 * q) = b * s;
+      }
+    }
+  };
+  run(nBlocks - 1 - pair);
+  if (PAIRED && pair != nBlocks - 1 - pair) run(pair);
 }
 
 // -------------------------------------------------------------------------
 // Key launch: dK and dV^T of query head h's contribution.  Workgroup = kNW
 // waves x 32 keys of K/V head h / G.
 // -------------------------------------------------------------------------
-template <bool VT_VEC>
+template <bool VT_VEC, bool PAIRED>
 __global__ void __launch_bounds__(64 * kNW, 2)
 sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
                   const half_t* __restrict__ Vt, const half_t* __restrict__ dO,
                   const float* __restrict__ L, const float* __restrict__ D,
                   float* __restrict__ dKp, float* __restrict__ dVp, float c, float s, int T,
-                  int Hq, int G, int nBlocks) {
+                  int Hq, int G, int nBlocks, int nPairs) {
   __shared__ __attribute__((aligned(16))) half_t smem[4 * kTileHalfs];
   __shared__ __attribute__((aligned(16))) float rowterms[2][2][kTile];  // [buf][L, D][query]
   half_t* const qbuf = smem;                    // Q tiles [2][64 queries][72]
@@ -367,194 +375,200 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
   const int n = lane & 31;
   const int g = lane >> 5;
 
-  // K/V head first, then key blocks heaviest (first) first, then the group's heads
+  // K/V head first, then key blocks heaviest first (paired: heavy block p,
+  // then light block nBlocks-1-p, so every workgroup carries the same causal
+  // work), then the group's heads
   const int lid = xcd_order();
-  const int kv = lid / (nBlocks * G);
-  const int rem = lid - kv * nBlocks * G;
-  const int blk = rem / G;
+  const int kv = lid / (nPairs * G);
+  const int rem = lid - kv * nPairs * G;
+  const int pair = rem / G;
   const int h = kv * G + rem % G;
-  const int key0 = blk * 32 * kNW;
-  const int waveKey0 = key0 + 32 * wave;
-  const int key = waveKey0 + n;
-  const bool live = key < T;
-  const int ft = key0 / kTile;                  // first query tile (key0 is a multiple of 64)
-  const int nt = (T + kTile - 1) / kTile;
+  auto run = [&](int blk) {
+    const int key0 = blk * 32 * kNW;
+    const int waveKey0 = key0 + 32 * wave;
+    const int key = waveKey0 + n;
+    const bool live = key < T;
+    const int ft = key0 / kTile;                  // first query tile (key0 is a multiple of 64)
+    const int nt = (T + kTile - 1) / kTile;
 
-  // K and V rows of the wave's keys as B operands (lane: key n, d = 16kk + 8g .. +7)
-  half8 kf[4], vf[4];
-  {
-    const half_t* krow_p = K + ((size_t)kv * T + key) * kD + 8 * g;
-    const half_t* vcol = Vt + (size_t)kv * kD * T + key;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      kf[kk] = live ? ld8(krow_p + 16 * kk) : half8{};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vf[kk][e] = live ? vcol[(size_t)(16 * kk + 8 * g + e) * T] : (half_t)0;
-    }
-  }
-
-  // Staging: thread t owns 16-byte chunks t and t + 256 of the Q tile and of
-  // the dO tile (row c/8, column chunk c%8); threads 0..63 the tile's L and
-  // threads 64..127 its -D (rows past T read L = +inf and -D = 0, so P = 0).
-  const int cr = tid >> 3, cc = tid & 7;
-  const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<half_t*>(Q + (size_t)h * T * kD), 0, T * kD * 2, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<half_t*>(dO + (size_t)h * kD), 0, (T * Hq - h) * kD * 2, kBufferWord3);
-  // Two register sets by tile parity, loads two tiles ahead (as in the query
-  // launch); tiles past the end read as zeros and their row terms as L = +inf,
-  // -D = 0.
-  int4v qst[2][2], ost[2][2];  // [set][chunk]
-  float rst[2] = {0.0f, 0.0f};
-  auto load = [&](int it, int set) {
-    const int q0 = it * kTile;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int r = q0 + cr + 32 * p;
-      qst[set][p] = __builtin_amdgcn_raw_buffer_load_b128(qrsrc, (r * kD + cc * 8) * 2, 0, 0);
-      ost[set][p] = __builtin_amdgcn_raw_buffer_load_b128(
-          orsrc, (int)(((unsigned)r * (unsigned)Hq * kD + cc * 8) * 2u), 0, 0);
-    }
-    if (tid < 2 * kTile) {
-      const int q = q0 + (tid & (kTile - 1));
-      const bool isL = tid < kTile;
-      rst[set] = q < T ? (isL ? L[(size_t)h * T + q] : -D[(size_t)h * T + q]) : (isL ? INFINITY : 0.0f);
-    }
-  };
-  auto store = [&](int buf, int set) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int off = buf * kTileHalfs + chunk_offset(cr + 32 * p, cc);
-      *reinterpret_cast<int4v*>(qbuf + off) = qst[set][p];
-      *reinterpret_cast<int4v*>(obuf + off) = ost[set][p];
-    }
-    if (tid < 2 * kTile) rowterms[buf][tid >> 6][tid & (kTile - 1)] = rst[set];
-  };
-
-  // natural Q / dO rows (queries krow(n), d = 16kk + 8g ..)
-  int nOff[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) nOff[kk] = chunk_offset(krow(n), 2 * kk + g);
-  // Q^T / dO^T rows (d = n + 32 mh)
-  int tOff[2][2];
-#pragma unroll
-  for (int mh = 0; mh < 2; ++mh)
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi) tOff[mh][hi] = tr_offset(lane, false, mh, hi);
-
-  float16v dk0 = {}, dk1 = {}, dv0 = {}, dv1 = {};
-  load(ft, 0);
-  load(ft + 1, 1);
-  store(0, 0);
-  __builtin_amdgcn_s_waitcnt(kLdsDone);
-  barrier();
-  auto tile_step = [&](int it, int buf) {
-    load(it + 2, buf);
-    if (it * kTile + kTile - 1 >= waveKey0) {
-      const half_t* qb = qbuf + buf * kTileHalfs;
-      const half_t* ob = obuf + buf * kTileHalfs;
-      // -D of element i's query 16(i/8) + 8g + i%8 (+32 for x1): the dP
-      // accumulators start there, so they end as dP - D
-      const float* lt = rowterms[buf][0];
-      const float* dt = rowterms[buf][1];
-      float16v nd0, nd1;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float4v d0 = *reinterpret_cast<const float4v*>(dt + 16 * b + 8 * g);
-        const float4v d1 = *reinterpret_cast<const float4v*>(dt + 16 * b + 8 * g + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float16v& nd = b < 2 ? nd0 : nd1;
-          nd[8 * (b & 1) + e] = d0[e];
-          nd[8 * (b & 1) + 4 + e] = d1[e];
-        }
-      }
-      // S = Q K^T and dP = dO V^T: queries 0..31 (x0) and 32..63 (x1) of the tile
-      float16v s0, s1, p0, p1;
-#pragma unroll
+    // K and V rows of the wave's keys as B operands (lane: key n, d = 16kk + 8g .. +7)
+    half8 kf[4], vf[4];
+    {
+      const half_t* krow_p = K + ((size_t)kv * T + key) * kD + 8 * g;
+      const half_t* vcol = Vt + (size_t)kv * kD * T + key;
+  #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const half8 a0 = ld8(qb + nOff[kk]);
-        const half8 a1 = ld8(qb + nOff[kk] + 32 * kRowHalfs);
-        s0 = mfma(a0, kf[kk], kk == 0 ? float16v{} : s0);
-        s1 = mfma(a1, kf[kk], kk == 0 ? float16v{} : s1);
-        const half8 b0 = ld8(ob + nOff[kk]);
-        const half8 b1 = ld8(ob + nOff[kk] + 32 * kRowHalfs);
-        p0 = mfma(b0, vf[kk], kk == 0 ? nd0 : p0);
-        p1 = mfma(b1, vf[kk], kk == 0 ? nd1 : p1);
-      }
-      // the diagonal: query 64it + 16(i/8) + 8g + i%8 (+32) is kept iff >= key
-      if (it * kTile < waveKey0 + 31) {
-        const int lim = key - it * kTile - 8 * g;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int q = 16 * (i >> 3) + (i & 7);
-          if (q < lim) s0[i] = -INFINITY;
-          if (q + 32 < lim) s1[i] = -INFINITY;
-        }
-      }
-      // P = 2^(S c - L) and dS = P (dP - D), eight queries at a time: block
-      // b holds queries 16b + 8g .. +7 of the tile (elements 8(b%2) .. of x(b/2))
-      half8 pb[4], db[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int q = 16 * b + 8 * g;
-        const float4v l0 = *reinterpret_cast<const float4v*>(lt + q);
-        const float4v l1 = *reinterpret_cast<const float4v*>(lt + q + 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = 8 * (b & 1) + e;
-          const float sv = b < 2 ? s0[i] : s1[i];
-          const float pv = b < 2 ? p0[i] : p1[i];
-          const float lv = e < 4 ? l0[e] : l1[e - 4];
-          const float P = __builtin_amdgcn_exp2f(fmaf(sv, c, -lv));
-          pb[b][e] = (half_t)P;
-          db[b][e] = (half_t)(P * pv);
-        }
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS: d = n (x0) and 32 + n (x1),
-      // queries 16ck + 8g .. +7
-#pragma unroll
-      for (int ck = 0; ck < 4; ++ck) {
-        const half_t* oc = ob + 16 * ck * kRowHalfs;
-        const half_t* qc = qb + 16 * ck * kRowHalfs;
-        const half8 o0 = tr8(oc, tOff[0][0], tOff[0][1]);
-        const half8 o1 = tr8(oc, tOff[1][0], tOff[1][1]);
-        dv0 = mfma(o0, pb[ck], dv0);
-        dv1 = mfma(o1, pb[ck], dv1);
-        const half8 q0 = tr8(qc, tOff[0][0], tOff[0][1]);
-        const half8 q1 = tr8(qc, tOff[1][0], tOff[1][1]);
-        dk0 = mfma(q0, db[ck], dk0);
-        dk1 = mfma(q1, db[ck], dk1);
+        kf[kk] = live ? ld8(krow_p + 16 * kk) : half8{};
+  #pragma unroll
+        for (int e = 0; e < 8; ++e)
+          vf[kk][e] = live ? vcol[(size_t)(16 * kk + 8 * g + e) * T] : (half_t)0;
       }
     }
-    store(buf ^ 1, buf ^ 1);
+
+    // Staging: thread t owns 16-byte chunks t and t + 256 of the Q tile and of
+    // the dO tile (row c/8, column chunk c%8); threads 0..63 the tile's L and
+    // threads 64..127 its -D (rows past T read L = +inf and -D = 0, so P = 0).
+    const int cr = tid >> 3, cc = tid & 7;
+    const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<half_t*>(Q + (size_t)h * T * kD), 0, T * kD * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<half_t*>(dO + (size_t)h * kD), 0, (T * Hq - h) * kD * 2, kBufferWord3);
+    // Two register sets by tile parity, loads two tiles ahead (as in the query
+    // launch); tiles past the end read as zeros and their row terms as L = +inf,
+    // -D = 0.
+    int4v qst[2][2], ost[2][2];  // [set][chunk]
+    float rst[2] = {0.0f, 0.0f};
+    auto load = [&](int it, int set) {
+      const int q0 = it * kTile;
+  #pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int r = q0 + cr + 32 * p;
+        qst[set][p] = __builtin_amdgcn_raw_buffer_load_b128(qrsrc, (r * kD + cc * 8) * 2, 0, 0);
+        ost[set][p] = __builtin_amdgcn_raw_buffer_load_b128(
+            orsrc, (int)(((unsigned)r * (unsigned)Hq * kD + cc * 8) * 2u), 0, 0);
+      }
+      if (tid < 2 * kTile) {
+        const int q = q0 + (tid & (kTile - 1));
+        const bool isL = tid < kTile;
+        rst[set] = q < T ? (isL ? L[(size_t)h * T + q] : -D[(size_t)h * T + q]) : (isL ? INFINITY : 0.0f);
+      }
+    };
+    auto store = [&](int buf, int set) {
+  #pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int off = buf * kTileHalfs + chunk_offset(cr + 32 * p, cc);
+        *reinterpret_cast<int4v*>(qbuf + off) = qst[set][p];
+        *reinterpret_cast<int4v*>(obuf + off) = ost[set][p];
+      }
+      if (tid < 2 * kTile) rowterms[buf][tid >> 6][tid & (kTile - 1)] = rst[set];
+    };
+
+    // natural Q / dO rows (queries krow(n), d = 16kk + 8g ..)
+    int nOff[4];
+  #pragma unroll
+    for (int kk = 0; kk < 4; ++kk) nOff[kk] = chunk_offset(krow(n), 2 * kk + g);
+    // Q^T / dO^T rows (d = n + 32 mh)
+    int tOff[2][2];
+  #pragma unroll
+    for (int mh = 0; mh < 2; ++mh)
+  #pragma unroll
+      for (int hi = 0; hi < 2; ++hi) tOff[mh][hi] = tr_offset(lane, false, mh, hi);
+
+    float16v dk0 = {}, dk1 = {}, dv0 = {}, dv1 = {};
+    load(ft, 0);
+    load(ft + 1, 1);
+    store(0, 0);
     __builtin_amdgcn_s_waitcnt(kLdsDone);
     barrier();
-  };
-  for (int it = ft; it < nt; it += 2) {  // unrolled by two: the sets are fixed registers
-    tile_step(it, 0);
-    if (it + 1 < nt) tile_step(it + 1, 1);
-  }
+    auto tile_step = [&](int it, int buf) {
+      load(it + 2, buf);
+      if (it * kTile + kTile - 1 >= waveKey0) {
+        const half_t* qb = qbuf + buf * kTileHalfs;
+        const half_t* ob = obuf + buf * kTileHalfs;
+        // -D of element i's query 16(i/8) + 8g + i%8 (+32 for x1): the dP
+        // accumulators start there, so they end as dP - D
+        const float* lt = rowterms[buf][0];
+        const float* dt = rowterms[buf][1];
+        float16v nd0, nd1;
+  #pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float4v d0 = *reinterpret_cast<const float4v*>(dt + 16 * b + 8 * g);
+          const float4v d1 = *reinterpret_cast<const float4v*>(dt + 16 * b + 8 * g + 4);
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float16v& nd = b < 2 ? nd0 : nd1;
+            nd[8 * (b & 1) + e] = d0[e];
+            nd[8 * (b & 1) + 4 + e] = d1[e];
+          }
+        }
+        // S = Q K^T and dP = dO V^T: queries 0..31 (x0) and 32..63 (x1) of the tile
+        float16v s0, s1, p0, p1;
+  #pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const half8 a0 = ld8(qb + nOff[kk]);
+          const half8 a1 = ld8(qb + nOff[kk] + 32 * kRowHalfs);
+          s0 = mfma(a0, kf[kk], kk == 0 ? float16v{} : s0);
+          s1 = mfma(a1, kf[kk], kk == 0 ? float16v{} : s1);
+          const half8 b0 = ld8(ob + nOff[kk]);
+          const half8 b1 = ld8(ob + nOff[kk] + 32 * kRowHalfs);
+          p0 = mfma(b0, vf[kk], kk == 0 ? nd0 : p0);
+          p1 = mfma(b1, vf[kk], kk == 0 ? nd1 : p1);
+        }
+        // the diagonal: query 64it + 16(i/8) + 8g + i%8 (+32) is kept iff >= key
+        if (it * kTile < waveKey0 + 31) {
+          const int lim = key - it * kTile - 8 * g;
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int q = 16 * (i >> 3) + (i & 7);
+            if (q < lim) s0[i] = -INFINITY;
+            if (q + 32 < lim) s1[i] = -INFINITY;
+          }
+        }
+        // P = 2^(S c - L) and dS = P (dP - D), eight queries at a time: block
+        // b holds queries 16b + 8g .. +7 of the tile (elements 8(b%2) .. of x(b/2))
+        half8 pb[4], db[4];
+  #pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int q = 16 * b + 8 * g;
+          const float4v l0 = *reinterpret_cast<const float4v*>(lt + q);
+          const float4v l1 = *reinterpret_cast<const float4v*>(lt + q + 4);
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int i = 8 * (b & 1) + e;
+            const float sv = b < 2 ? s0[i] : s1[i];
+            const float pv = b < 2 ? p0[i] : p1[i];
+            const float lv = e < 4 ? l0[e] : l1[e - 4];
+            const float P = __builtin_amdgcn_exp2f(fmaf(sv, c, -lv));
+            pb[b][e] = (half_t)P;
+            db[b][e] = (half_t)(P * pv);
+          }
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS: d = n (x0) and 32 + n (x1),
+        // queries 16ck + 8g .. +7
+  #pragma unroll
+        for (int ck = 0; ck < 4; ++ck) {
+          const half_t* oc = ob + 16 * ck * kRowHalfs;
+          const half_t* qc = qb + 16 * ck * kRowHalfs;
+          const half8 o0 = tr8(oc, tOff[0][0], tOff[0][1]);
+          const half8 o1 = tr8(oc, tOff[1][0], tOff[1][1]);
+          dv0 = mfma(o0, pb[ck], dv0);
+          dv1 = mfma(o1, pb[ck], dv1);
+          const half8 q0 = tr8(qc, tOff[0][0], tOff[0][1]);
+          const half8 q1 = tr8(qc, tOff[1][0], tOff[1][1]);
+          dk0 = mfma(q0, db[ck], dk0);
+          dk1 = mfma(q1, db[ck], dk1);
+        }
+      }
+      store(buf ^ 1, buf ^ 1);
+      __builtin_amdgcn_s_waitcnt(kLdsDone);
+      barrier();
+    };
+    for (int it = ft; it < nt; it += 2) {  // unrolled by two: the sets are fixed registers
+      tile_step(it, 0);
+      if (it + 1 < nt) tile_step(it + 1, 1);
+    }
 
-  // accumulator element 4q + e of lane (n, g) is d = 8q + 4g + e of key n
-  if (live) {
-    float* kout = dKp + ((size_t)h * T + key) * kD + 4 * g;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4v a = {dk0[4 * q], dk0[4 * q + 1], dk0[4 * q + 2], dk0[4 * q + 3]};
-      const float4v b = {dk1[4 * q], dk1[4 * q + 1], dk1[4 * q + 2], dk1[4 * q + 3]};
-      *reinterpret_cast<float4v*>(kout + 8 * q) = a * s;
-      *reinterpret_cast<float4v*>(kout + 32 + 8 * q) = b * s;
+    // accumulator element 4q + e of lane (n, g) is d = 8q + 4g + e of key n
+    if (live) {
+      float* kout = dKp + ((size_t)h * T + key) * kD + 4 * g;
+  #pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4v a = {dk0[4 * q], dk0[4 * q + 1], dk0[4 * q + 2], dk0[4 * q + 3]};
+        const float4v b = {dk1[4 * q], dk1[4 * q + 1], dk1[4 * q + 2], dk1[4 * q + 3]};
+        *reinterpret_cast<float4v*>(kout + 8 * q) = a * s;
+        *reinterpret_cast<float4v*>(kout + 32 + 8 * q) = b * s;
+      }
+      float* vout = dVp + (size_t)h * kD * T + key;
+  #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int d = 8 * (i >> 2) + 4 * g + (i & 3);
+        vout[(size_t)d * T] = dv0[i];
+        vout[(size_t)(d + 32) * T] = dv1[i];
+      }
     }
-    float* vout = dVp + (size_t)h * kD * T + key;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int d = 8 * (i >> 2) + 4 * g + (i & 3);
-      vout[(size_t)d * T] = dv0[i];
-      vout[(size_t)(d + 32) * T] = dv1[i];
-    }
-  }
+  };
+  run(pair);
+  if (PAIRED && pair != nBlocks - 1 - pair) run(nBlocks - 1 - pair);
 }
 
 // -------------------------------------------------------------------------
@@ -594,17 +608,25 @@ int check_device() {
   return ok ? SATTN_OK : SATTN_ERR_DEVICE;
 }
 
+// Heavy/light pairing halves the grid; it pays when the halved grid still
+// gives every compute unit (256 of them) a workgroup, and otherwise the idle
+// units cost more than the imbalance it removes.
+bool pair_blocks(int nBlocks, int Hq) {
+  return nBlocks > 1 && (long long)((nBlocks + 1) / 2) * Hq >= 256;
+}
+
 void launch_query(const half_t* Q, const half_t* K, const half_t* Vt, const half_t* O,
                   const half_t* dO, const float* L, float* dQ, float* D, float c, float s, int T,
                   int Hq, int Hkv, hipStream_t stream) {
   const int nBlocks = (T + 32 * kNW - 1) / (32 * kNW);
-  const dim3 grid((unsigned)nBlocks * (unsigned)Hq);
-  if (T % 8 == 0)
-    hipLaunchKernelGGL(sattn_bwdq_kernel<true>, grid, dim3(64 * kNW), 0, stream, Q, K, Vt, O, dO,
-                       L, dQ, D, c, s, T, Hq, Hq / Hkv, nBlocks);
-  else
-    hipLaunchKernelGGL(sattn_bwdq_kernel<false>, grid, dim3(64 * kNW), 0, stream, Q, K, Vt, O, dO,
-                       L, dQ, D, c, s, T, Hq, Hq / Hkv, nBlocks);
+  const bool paired = pair_blocks(nBlocks, Hq);
+  const int nPairs = paired ? (nBlocks + 1) / 2 : nBlocks;
+  const dim3 grid((unsigned)nPairs * (unsigned)Hq);
+  const int G = Hq / Hkv;
+  auto kernel = paired ? sattn_bwdq_kernel<true, true> : sattn_bwdq_kernel<true, false>;
+  if (T % 8 != 0) kernel = paired ? sattn_bwdq_kernel<false, true> : sattn_bwdq_kernel<false, false>;
+  hipLaunchKernelGGL(kernel, grid, dim3(64 * kNW), 0, stream, Q, K, Vt, O, dO, L, dQ, D, c, s, T, Hq,
+                     G, nBlocks, nPairs);
 }
 
 void launch_key(const half_t* Q, const half_t* K, const half_t* Vt, const half_t* dO,
@@ -614,9 +636,12 @@ void launch_key(const half_t* Q, const half_t* K, const half_t* Vt, const half_t
   float* kp = G == 1 ? dK : static_cast<float*>(ws);
   float* vp = G == 1 ? dVt : static_cast<float*>(ws) + (size_t)Hq * T * kD;
   const int nBlocks = (T + 32 * kNW - 1) / (32 * kNW);
-  const dim3 grid((unsigned)nBlocks * (unsigned)Hq);
-  hipLaunchKernelGGL(sattn_bwdk_kernel<true>, grid, dim3(64 * kNW), 0, stream, Q, K, Vt, dO, L, D,
-                     kp, vp, c, s, T, Hq, G, nBlocks);
+  const bool paired = pair_blocks(nBlocks, Hq);
+  const int nPairs = paired ? (nBlocks + 1) / 2 : nBlocks;
+  const dim3 grid((unsigned)nPairs * (unsigned)Hq);
+  const auto kernel = paired ? sattn_bwdk_kernel<true, true> : sattn_bwdk_kernel<true, false>;
+  hipLaunchKernelGGL(kernel, grid, dim3(64 * kNW), 0, stream, Q, K, Vt, dO, L, D, kp, vp, c, s, T,
+                     Hq, G, nBlocks, nPairs);
   if (G > 1) {
     const int planeQuads = T * kD / 4;
     const dim3 rgrid((unsigned)((planeQuads + 255) / 256), (unsigned)Hkv, 2u);
