@@ -6,6 +6,11 @@ line: causal TFLOP/s (4*T^2*64*Hq/2 flop per call), the roofline of the
 kernel against the fp16 dense MFMA peak, and the float64 CPU oracle timed on
 a bounded sample of the same workload.
 
+After the timed region the kernel runs back-to-back for about a second
+while a host thread reads the shader clock through amdsmi; the line's
+"clock" object gives it and the fraction of the fp16 peak scaled to it (the
+card is held below 2.4 GHz by board power under matrix work on random data).
+
 With --backward, one step is one sattn_bwd call (query launch, key launch,
 grouped reduction) on the same workload, with dO seeded and O and L from the
 forward; its line counts the five products S, dP, dQ, dK, dV once each
@@ -76,6 +81,70 @@ def cpu_baseline(x, budget_s=20.0):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{heads} of {x.Hq} query heads of T={x.T} Hq={x.Hq} Hkv={x.Hkv} "
                       f"({dt:.1f} s, float64 NumPy)"}
+
+
+def gfx_clock_window(torch, fn, seconds=1.0):
+    """The shader clock while ``fn`` runs back-to-back for about ``seconds``
+    (after the timed region, so the timing is undisturbed): the median of
+    amdsmi's per-XCD current GFX clocks, read every 50 ms from a host thread
+    once the first 0.2 s have passed.  None when amdsmi cannot read them."""
+    try:
+        import threading
+        import amdsmi
+        amdsmi.amdsmi_init()
+        bus = torch.cuda.get_device_properties(0).pci_bus_id
+        handle = None
+        for h in amdsmi.amdsmi_get_processor_handles():
+            if int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == bus:
+                handle = h
+        if handle is None:
+            return None
+    except Exception:
+        return None
+    samples = []
+    stop = threading.Event()
+
+    def sample():
+        stop.wait(0.2)
+        while not stop.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+                clks = [v for v in (m.get("current_gfxclks") or []) if isinstance(v, (int, float))]
+                if not clks and isinstance(m.get("current_gfxclk"), (int, float)):
+                    clks = [m["current_gfxclk"]]
+                if clks:
+                    samples.append(sum(clks) / len(clks))
+            except Exception:
+                pass
+            stop.wait(0.05)
+
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds + 0.2:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    if not samples:
+        return None
+    samples.sort()
+    return {"gfx_mhz": round(samples[len(samples) // 2], 1), "samples": len(samples),
+            "source": "amdsmi current GFX clock (mean of the XCDs), median over the samples "
+                      "taken while the kernel ran back-to-back after the timed region"}
+
+
+def clock_fields(clock, achieved):
+    """The fraction of the fp16 dense peak scaled to the measured clock."""
+    if clock is None:
+        return None
+    peak = PEAK_FP16_TFLOPS * clock["gfx_mhz"] / 2400.0
+    return {**clock, "peak_at_clock": round(peak, 1), "frac_at_clock": round(achieved / peak, 4)}
 
 
 def backward_flops(T, Hq, d=64):
@@ -199,6 +268,8 @@ def bench_backward(args, torch, sattn, x, w):
                      "traffic": None, "kernel": "key launch + reduction (4 products)",
                      "kernel_ms": round(key_ms, 5)},
     }
+    if not args.no_clock:
+        out["clock"] = clock_fields(gfx_clock_window(torch, step), value)
     if not args.no_cpu_baseline:
         O_np = O.cpu().numpy()
         L_np = L.cpu().numpy()
@@ -425,6 +496,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=300,
                     help="untimed calls first; the GPU needs a few tens of ms of load to reach its working clock")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the shader-clock window (amdsmi) after the timed region")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline line, one JSON line per synthetic workload "
@@ -442,7 +515,7 @@ def main():
                          "(the reference transfer for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
@@ -559,6 +632,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
                      "traffic": traffic, "kernel_ms": round(kernel_ms, 5)},
     }
+    if not args.no_clock:
+        out["clock"] = clock_fields(gfx_clock_window(torch, step), achieved)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)
     print(json.dumps(out), flush=True)

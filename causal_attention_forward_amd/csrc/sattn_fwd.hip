@@ -399,6 +399,26 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
 #pragma unroll
       for (int i = 0; i < 4; ++i) r[i] = rd(i);
       float acc[4];
+      // Softmax software-pipelined across the 16 slots: slot i exponentiates
+      // the two arguments formed in slot i-1, forms those of slot i+1 and
+      // sums the two P of slot i-1, so no instruction waits on the one
+      // issued just before it.
+      auto el = [&](int e) -> float { return e < 16 ? s0[e] : s1[e - 16]; };
+      auto set = [&](int e, float v) {
+        if (e < 16) s0[e] = v;
+        else s1[e - 16] = v;
+      };
+      float ta = __builtin_fmaf(el(0), c, neg_m), tb = __builtin_fmaf(el(1), c, neg_m);
+      auto finish = [&](int i) {  // sum and pack the P of slot i
+        const float t = el(2 * i) + el(2 * i + 1);
+        acc[i & 3] = i < 4 ? t : acc[i & 3] + t;
+        if ((i & 3) == 3) {
+          const float16v& sv = i < 8 ? s0 : s1;  // binary16 P of keys 8(i/4 % 2) + 0..7
+          const float8v v8 = (i & 4) ? __builtin_shufflevector(sv, sv, 8, 9, 10, 11, 12, 13, 14, 15)
+                                     : __builtin_shufflevector(sv, sv, 0, 1, 2, 3, 4, 5, 6, 7);
+          pout[i >> 2] = to_half8(v8);
+        }
+      };
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -414,26 +434,16 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
           }
           if (i + 4 < kM) r[i & 3] = rd(i + 4);
         }
-        // softmax of elements 2i, 2i+1 (s0 for i < 8, s1 after)
-        float t;
-        if (i < 8) {
-          s0[2 * i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[2 * i], c, neg_m));
-          s0[2 * i + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[2 * i + 1], c, neg_m));
-          t = s0[2 * i] + s0[2 * i + 1];
-        } else {
-          s1[2 * i - 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[2 * i - 16], c, neg_m));
-          s1[2 * i - 15] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[2 * i - 15], c, neg_m));
-          t = s1[2 * i - 16] + s1[2 * i - 15];
+        set(2 * i, __builtin_amdgcn_exp2f(ta));
+        set(2 * i + 1, __builtin_amdgcn_exp2f(tb));
+        if (i < 15) {
+          ta = __builtin_fmaf(el(2 * i + 2), c, neg_m);
+          tb = __builtin_fmaf(el(2 * i + 3), c, neg_m);
         }
-        acc[i & 3] = i < 4 ? t : acc[i & 3] + t;
-        if ((i & 3) == 3) {
-          const float16v& sv = i < 8 ? s0 : s1;  // binary16 P of keys 8(i/4 % 2) + 0..7
-          const float8v v8 = (i & 4) ? __builtin_shufflevector(sv, sv, 8, 9, 10, 11, 12, 13, 14, 15)
-                                     : __builtin_shufflevector(sv, sv, 0, 1, 2, 3, 4, 5, 6, 7);
-          pout[i >> 2] = to_half8(v8);
-        }
+        if (i > 0) finish(i - 1);
         __builtin_amdgcn_sched_barrier(0);
       }
+      finish(15);
       float lsum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
       const bool over = __builtin_amdgcn_ballot_w64(!(lsum <= kSumCap)) != 0;
       // Pins the binary16 P in this block: the fp32 P dies here on the fast
