@@ -33,12 +33,12 @@
 //    forward's own layouts (Q, K, V^T, token-major O) and no transposed copy
 //    of anything is written to memory.
 //  * A wave owns 32 queries (query launch) or 32 keys (key launch); a
-//    workgroup is four waves on consecutive rows and stages each 64-row tile
-//    once for all of them, loaded two tiles ahead.  A workgroup takes a heavy
-//    block and then its light partner (blocks b and n-1-b), so every
-//    workgroup carries the same causal work; each XCD receives a contiguous
-//    run of workgroups ordered K/V head first (that head's tiles stay in its
-//    L2).
+//    workgroup is eight (or, on small grids, four) waves on consecutive rows
+//    and stages each 64-row tile once for all of them, loaded two tiles
+//    ahead.  On large grids a workgroup takes a heavy block and then its
+//    light partner (blocks b and n-1-b), so every workgroup carries the same
+//    causal work; each XCD receives a contiguous run of workgroups ordered
+//    K/V head first (that head's tiles stay in its L2).
 //  * With GQA the key launch writes one dK and one dV^T plane per query head
 //    into a caller-provided workspace and a reduction sums the G planes of
 //    each K/V head in head order; with Hq == Hkv it writes dK and dV^T
@@ -68,7 +68,6 @@ constexpr int kRowHalfs = kD;                   // LDS row: 64 values, 16-byte c
 constexpr int kTileHalfs = kTile * kRowHalfs;
 constexpr int kBufferWord3 = 0x00020000;        // raw buffer, 32-bit data format
 constexpr int kOutOfRange = 0x7FFFFFF0;         // a buffer offset past every range
-constexpr int kNW = 4;                          // waves per workgroup
 constexpr int kXcds = 8;                        // accelerator complex dies per MI355X
 
 // Workgroups are dealt to the eight XCDs round-robin by index.  This returns
@@ -161,10 +160,10 @@ __device__ __forceinline__ half8 pack8(const float16v& x, int h) {
 }
 
 // -------------------------------------------------------------------------
-// Query launch: D and dQ.  Workgroup = kNW waves x 32 query rows of head h.
+// Query launch: D and dQ.  Workgroup = NW waves x 32 query rows of head h.
 // -------------------------------------------------------------------------
-template <bool VT_VEC, bool PAIRED>
-__global__ void __launch_bounds__(64 * kNW, 2)
+template <int NW, bool VT_VEC, bool PAIRED>
+__global__ void __launch_bounds__(64 * NW, 8 / NW)
 sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
                   const half_t* __restrict__ Vt, const half_t* __restrict__ O,
                   const half_t* __restrict__ dO, const float* __restrict__ L,
@@ -189,11 +188,11 @@ sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
   const int pair = rem / G;
   const int h = kv * G + rem % G;
   auto run = [&](int blk) {
-    const int row0 = blk * 32 * kNW;
+    const int row0 = blk * 32 * NW;
     const int waveRow0 = row0 + 32 * wave;
     const int row = waveRow0 + n;
     const bool live = row < T;
-    const int nkt = min(T - 1, row0 + 32 * kNW - 1) / kTile + 1;  // key tiles of the workgroup
+    const int nkt = min(T - 1, row0 + 32 * NW - 1) / kTile + 1;  // key tiles of the workgroup
     const int waveLast = min(T - 1, waveRow0 + 31);               // the wave's last row
 
     // Q and dO rows as B operands (lane: row n, columns 16kk + 8g .. +7), and D.
@@ -219,8 +218,9 @@ sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
     for (int i = 0; i < 16; ++i) negD[i] = -Drow;
     if (live && g == 0) D[(size_t)h * T + row] = Drow;
 
-    // Staging: thread t owns 16-byte chunks t and t + 256 of a K tile (row
+    // Staging: thread t owns 16-byte chunks t, t + 64 NW, .. of a K tile (row
     // c/8, column chunk c%8) and of a V^T tile.
+    constexpr int kCpt = 512 / (64 * NW), kRowStep = 8 * NW;  // chunks per thread, rows between them
     const int cr = tid >> 3, cc = tid & 7;
     const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<half_t*>(K + (size_t)kv * T * kD), 0, T * kD * 2, kBufferWord3);
@@ -231,12 +231,12 @@ sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
     // stored at step kt + 1, so its loads have a whole step to arrive.  Tiles
     // past the end read as zeros (range checks), so every step issues the same
     // loads and stores and the compiler's load waits stay exact.
-    int4v kst[2][2], vst[2][2];  // [set][chunk]
+    int4v kst[2][kCpt], vst[2][kCpt];  // [set][chunk]
     auto load = [&](int kt, int set) {
       const int key0 = kt * kTile;
   #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int r = cr + 32 * p;
+      for (int p = 0; p < kCpt; ++p) {
+        const int r = cr + kRowStep * p;
         kst[set][p] = __builtin_amdgcn_raw_buffer_load_b128(krsrc, ((key0 + r) * kD + cc * 8) * 2, 0, 0);
         if (VT_VEC) {
           const int off = key0 + cc * 8 < T ? (r * T + key0 + cc * 8) * 2 : kOutOfRange;
@@ -254,8 +254,8 @@ sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
     };
     auto store = [&](int buf, int set) {
   #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int off = buf * kTileHalfs + chunk_offset(cr + 32 * p, cc);
+      for (int p = 0; p < kCpt; ++p) {
+        const int off = buf * kTileHalfs + chunk_offset(cr + kRowStep * p, cc);
         *reinterpret_cast<int4v*>(kbuf + off) = kst[set][p];
         *reinterpret_cast<int4v*>(vbuf + off) = vst[set][p];
       }
@@ -354,11 +354,11 @@ sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
 }
 
 // -------------------------------------------------------------------------
-// Key launch: dK and dV^T of query head h's contribution.  Workgroup = kNW
+// Key launch: dK and dV^T of query head h's contribution.  Workgroup = NW
 // waves x 32 keys of K/V head h / G.
 // -------------------------------------------------------------------------
-template <bool VT_VEC, bool PAIRED>
-__global__ void __launch_bounds__(64 * kNW, 2)
+template <int NW, bool VT_VEC, bool PAIRED>
+__global__ void __launch_bounds__(64 * NW, 8 / NW)
 sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
                   const half_t* __restrict__ Vt, const half_t* __restrict__ dO,
                   const float* __restrict__ L, const float* __restrict__ D,
@@ -384,7 +384,7 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
   const int pair = rem / G;
   const int h = kv * G + rem % G;
   auto run = [&](int blk) {
-    const int key0 = blk * 32 * kNW;
+    const int key0 = blk * 32 * NW;
     const int waveKey0 = key0 + 32 * wave;
     const int key = waveKey0 + n;
     const bool live = key < T;
@@ -405,9 +405,11 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
       }
     }
 
-    // Staging: thread t owns 16-byte chunks t and t + 256 of the Q tile and of
-    // the dO tile (row c/8, column chunk c%8); threads 0..63 the tile's L and
-    // threads 64..127 its -D (rows past T read L = +inf and -D = 0, so P = 0).
+    // Staging: thread t owns 16-byte chunks t, t + 64 NW, .. of the Q tile and
+    // of the dO tile (row c/8, column chunk c%8); threads 0..63 the tile's L
+    // and threads 64..127 its -D (rows past T read L = +inf and -D = 0, so
+    // P = 0).
+    constexpr int kCpt = 512 / (64 * NW), kRowStep = 8 * NW;  // chunks per thread, rows between them
     const int cr = tid >> 3, cc = tid & 7;
     const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<half_t*>(Q + (size_t)h * T * kD), 0, T * kD * 2, kBufferWord3);
@@ -416,13 +418,13 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
     // Two register sets by tile parity, loads two tiles ahead (as in the query
     // launch); tiles past the end read as zeros and their row terms as L = +inf,
     // -D = 0.
-    int4v qst[2][2], ost[2][2];  // [set][chunk]
+    int4v qst[2][kCpt], ost[2][kCpt];  // [set][chunk]
     float rst[2] = {0.0f, 0.0f};
     auto load = [&](int it, int set) {
       const int q0 = it * kTile;
   #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int r = q0 + cr + 32 * p;
+      for (int p = 0; p < kCpt; ++p) {
+        const int r = q0 + cr + kRowStep * p;
         qst[set][p] = __builtin_amdgcn_raw_buffer_load_b128(qrsrc, (r * kD + cc * 8) * 2, 0, 0);
         ost[set][p] = __builtin_amdgcn_raw_buffer_load_b128(
             orsrc, (int)(((unsigned)r * (unsigned)Hq * kD + cc * 8) * 2u), 0, 0);
@@ -435,8 +437,8 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
     };
     auto store = [&](int buf, int set) {
   #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int off = buf * kTileHalfs + chunk_offset(cr + 32 * p, cc);
+      for (int p = 0; p < kCpt; ++p) {
+        const int off = buf * kTileHalfs + chunk_offset(cr + kRowStep * p, cc);
         *reinterpret_cast<int4v*>(qbuf + off) = qst[set][p];
         *reinterpret_cast<int4v*>(obuf + off) = ost[set][p];
       }
@@ -608,25 +610,38 @@ int check_device() {
   return ok ? SATTN_OK : SATTN_ERR_DEVICE;
 }
 
-// Heavy/light pairing halves the grid; it pays when the halved grid still
-// gives every compute unit (256 of them) a workgroup, and otherwise the idle
-// units cost more than the imbalance it removes.
-bool pair_blocks(int nBlocks, int Hq) {
-  return nBlocks > 1 && (long long)((nBlocks + 1) / 2) * Hq >= 256;
+// Launch shape.  Eight-wave workgroups (one per compute unit) stage each tile
+// once for 256 rows and run a heavy block, then its light partner (blocks b
+// and n-1-b), so every workgroup carries the same causal work; they are used
+// when that grid still gives each of the 256 compute units a workgroup.
+// Otherwise four-wave workgroups (two per compute unit) run, paired the same
+// way when their halved grid still fills the compute units, and else one
+// block each, heaviest first: idle units cost more than the imbalance.
+struct Shape {
+  int nw, nBlocks, nPairs;
+  bool paired;
+};
+Shape launch_shape(int T, int Hq) {
+  const int n8 = (T + 255) / 256, n4 = (T + 127) / 128;
+  if (n8 > 1 && (long long)((n8 + 1) / 2) * Hq >= 256) return {8, n8, (n8 + 1) / 2, true};
+  const bool paired = n4 > 1 && (long long)((n4 + 1) / 2) * Hq >= 256;
+  return {4, n4, paired ? (n4 + 1) / 2 : n4, paired};
 }
 
 void launch_query(const half_t* Q, const half_t* K, const half_t* Vt, const half_t* O,
                   const half_t* dO, const float* L, float* dQ, float* D, float c, float s, int T,
                   int Hq, int Hkv, hipStream_t stream) {
-  const int nBlocks = (T + 32 * kNW - 1) / (32 * kNW);
-  const bool paired = pair_blocks(nBlocks, Hq);
-  const int nPairs = paired ? (nBlocks + 1) / 2 : nBlocks;
-  const dim3 grid((unsigned)nPairs * (unsigned)Hq);
+  const Shape sh = launch_shape(T, Hq);
+  const dim3 grid((unsigned)sh.nPairs * (unsigned)Hq);
   const int G = Hq / Hkv;
-  auto kernel = paired ? sattn_bwdq_kernel<true, true> : sattn_bwdq_kernel<true, false>;
-  if (T % 8 != 0) kernel = paired ? sattn_bwdq_kernel<false, true> : sattn_bwdq_kernel<false, false>;
-  hipLaunchKernelGGL(kernel, grid, dim3(64 * kNW), 0, stream, Q, K, Vt, O, dO, L, dQ, D, c, s, T, Hq,
-                     G, nBlocks, nPairs);
+  const bool vec = T % 8 == 0;
+  auto kernel = vec ? sattn_bwdq_kernel<8, true, true> : sattn_bwdq_kernel<8, false, true>;
+  if (sh.nw == 4 && sh.paired)
+    kernel = vec ? sattn_bwdq_kernel<4, true, true> : sattn_bwdq_kernel<4, false, true>;
+  if (sh.nw == 4 && !sh.paired)
+    kernel = vec ? sattn_bwdq_kernel<4, true, false> : sattn_bwdq_kernel<4, false, false>;
+  hipLaunchKernelGGL(kernel, grid, dim3(64 * sh.nw), 0, stream, Q, K, Vt, O, dO, L, dQ, D, c, s, T,
+                     Hq, G, sh.nBlocks, sh.nPairs);
 }
 
 void launch_key(const half_t* Q, const half_t* K, const half_t* Vt, const half_t* dO,
@@ -635,13 +650,12 @@ void launch_key(const half_t* Q, const half_t* K, const half_t* Vt, const half_t
   const int G = Hq / Hkv;
   float* kp = G == 1 ? dK : static_cast<float*>(ws);
   float* vp = G == 1 ? dVt : static_cast<float*>(ws) + (size_t)Hq * T * kD;
-  const int nBlocks = (T + 32 * kNW - 1) / (32 * kNW);
-  const bool paired = pair_blocks(nBlocks, Hq);
-  const int nPairs = paired ? (nBlocks + 1) / 2 : nBlocks;
-  const dim3 grid((unsigned)nPairs * (unsigned)Hq);
-  const auto kernel = paired ? sattn_bwdk_kernel<true, true> : sattn_bwdk_kernel<true, false>;
-  hipLaunchKernelGGL(kernel, grid, dim3(64 * kNW), 0, stream, Q, K, Vt, dO, L, D, kp, vp, c, s, T,
-                     Hq, G, nBlocks, nPairs);
+  const Shape sh = launch_shape(T, Hq);
+  const dim3 grid((unsigned)sh.nPairs * (unsigned)Hq);
+  auto kernel = sattn_bwdk_kernel<8, true, true>;
+  if (sh.nw == 4) kernel = sh.paired ? sattn_bwdk_kernel<4, true, true> : sattn_bwdk_kernel<4, true, false>;
+  hipLaunchKernelGGL(kernel, grid, dim3(64 * sh.nw), 0, stream, Q, K, Vt, dO, L, D, kp, vp, c, s, T,
+                     Hq, G, sh.nBlocks, sh.nPairs);
   if (G > 1) {
     const int planeQuads = T * kD / 4;
     const dim3 rgrid((unsigned)((planeQuads + 255) / 256), (unsigned)Hkv, 2u);

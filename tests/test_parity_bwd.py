@@ -28,12 +28,14 @@ FULL = [
     (257, 2, 2, 57, {"qk_std": 1.5}),
     (1000, 16, 4, 2, {"peaked_fraction": 0.01}),
     (1024, 8, 8, 1, {"qk_std": 0.5, "v_std": 0.5}),
-    # grids large enough for heavy/light block pairing: odd block counts (the
-    # middle block pairs with itself), one with a non-multiple-of-8 tail, and
-    # an even count
+    # grids large enough for heavy/light block pairing: four-wave workgroups
+    # with an odd block count (the middle block pairs with itself) and a
+    # non-multiple-of-8 tail, and with an even count; eight-wave workgroups
+    # with an odd count, and with a non-multiple-of-8 tail
     (300, 128, 16, 61, {}),
-    (520, 128, 64, 62, {}),
     (512, 128, 16, 63, {}),
+    (520, 128, 64, 62, {}),
+    (777, 128, 64, 64, {}),
 ]
 
 
