@@ -31,28 +31,30 @@ PEAK_FP16_TFLOPS = 2516.6  # MI355X dense fp16 MFMA: 256 CU x 2.4 GHz x 4096 flo
 WORKLOAD_INDEX = 3
 KERNEL_SRC = os.path.join(ROOT, "causal_attention_forward_amd", "csrc", "sattn_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sattn_fwd_T4096_Hq32_Hkv8.txt")
+BWD_KERNEL_SRC = os.path.join(ROOT, "causal_attention_forward_amd", "csrc", "sattn_bwd.hip")
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sattn_bwd_T4096_Hq32_Hkv8.txt")
 
 
 def causal_flops(T, Hq, d=64):
     return 4.0 * T * T * d * Hq / 2.0
 
 
-def kernel_sha():
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_sha(src=KERNEL_SRC):
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+def measured_traffic(path=TRAFFIC_FILE, src=KERNEL_SRC):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or
     None when it is missing or was taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_sha") != kernel_sha():
+    if kv.get("kernel_sha") != kernel_sha(src):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -265,7 +267,9 @@ def bench_backward(args, torch, sattn, x, w):
                    "key_launch_and_reduction_ms": round(key_ms, 5)},
         "roofline": {"bound": "mfma", "achieved": round(key_tf, 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(key_tf / PEAK_FP16_TFLOPS, 4),
-                     "traffic": None, "kernel": "key launch + reduction (4 products)",
+                     "traffic": (measured_traffic(BWD_TRAFFIC_FILE, BWD_KERNEL_SRC)
+                                 if args.workload == WORKLOAD_INDEX else None),
+                     "kernel": "key launch + reduction (4 products)",
                      "kernel_ms": round(key_ms, 5)},
     }
     if not args.no_clock:

@@ -36,6 +36,12 @@ def test_traffic_summary_matches_the_kernel_source():
     assert 42467328 <= got <= 1.05 * 42467328
 
 
+def test_backward_traffic_summary_matches_the_kernel_source():
+    got = bench.measured_traffic(bench.BWD_TRAFFIC_FILE, bench.BWD_KERNEL_SRC)
+    assert got is not None, "profiles/ backward traffic summary is stale or missing"
+    assert 193986560 <= got <= 1.05 * 193986560
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
