@@ -6,10 +6,11 @@ line: causal TFLOP/s (4*T^2*64*Hq/2 flop per call), the roofline of the
 kernel against the fp16 dense MFMA peak, and the float64 CPU oracle timed on
 a bounded sample of the same workload.
 
-After the timed region the kernel runs back-to-back for about a second
-while a host thread reads the shader clock through amdsmi; the line's
-"clock" object gives it and the fraction of the fp16 peak scaled to it (the
-card is held below 2.4 GHz by board power under matrix work on random data).
+After the timed region the kernel runs back-to-back for about two seconds
+while a host thread reads the shader clock and socket power through amdsmi;
+the line's "clock" object gives them and the fraction of the fp16 peak
+scaled to that clock (the card is held below 2.4 GHz by board power under
+matrix work on random data).
 
 With --backward, one step is one sattn_bwd call (query launch, key launch,
 grouped reduction) on the same workload, with dO seeded and O and L from the
@@ -85,11 +86,14 @@ def cpu_baseline(x, budget_s=20.0):
                       f"({dt:.1f} s, float64 NumPy)"}
 
 
-def gfx_clock_window(torch, fn, seconds=1.0):
-    """The shader clock while ``fn`` runs back-to-back for about ``seconds``
-    (after the timed region, so the timing is undisturbed): the median of
-    amdsmi's per-XCD current GFX clocks, read every 50 ms from a host thread
-    once the first 0.2 s have passed.  None when amdsmi cannot read them."""
+def gfx_clock_window(torch, fn, settle=1.0, seconds=1.0):
+    """The shader clock while ``fn`` runs back-to-back (after the timed
+    region, so the timing is undisturbed): amdsmi's current GFX clock of each
+    XCD and the socket power, read every 20 ms from a host thread.  The
+    driver refreshes these readings only every few hundred ms, so the first
+    ``settle`` seconds (which can still show the idle clock) are discarded
+    and the readings of the next ``seconds`` averaged.  None when amdsmi
+    cannot read them."""
     try:
         import threading
         import amdsmi
@@ -103,11 +107,11 @@ def gfx_clock_window(torch, fn, seconds=1.0):
             return None
     except Exception:
         return None
-    samples = []
+    clocks, powers = [], []
     stop = threading.Event()
 
     def sample():
-        stop.wait(0.2)
+        stop.wait(settle)
         while not stop.is_set():
             try:
                 m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
@@ -115,15 +119,17 @@ def gfx_clock_window(torch, fn, seconds=1.0):
                 if not clks and isinstance(m.get("current_gfxclk"), (int, float)):
                     clks = [m["current_gfxclk"]]
                 if clks:
-                    samples.append(sum(clks) / len(clks))
+                    clocks.append(sum(clks) / len(clks))
+                if isinstance(m.get("current_socket_power"), (int, float)):
+                    powers.append(m["current_socket_power"])
             except Exception:
                 pass
-            stop.wait(0.05)
+            stop.wait(0.02)
 
     th = threading.Thread(target=sample, daemon=True)
     th.start()
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds + 0.2:
+    while time.perf_counter() - t0 < settle + seconds:
         for _ in range(20):
             fn()
         torch.cuda.synchronize()
@@ -133,12 +139,16 @@ def gfx_clock_window(torch, fn, seconds=1.0):
         amdsmi.amdsmi_shut_down()
     except Exception:
         pass
-    if not samples:
+    if not clocks:
         return None
-    samples.sort()
-    return {"gfx_mhz": round(samples[len(samples) // 2], 1), "samples": len(samples),
-            "source": "amdsmi current GFX clock (mean of the XCDs), median over the samples "
-                      "taken while the kernel ran back-to-back after the timed region"}
+    out = {"gfx_mhz": round(sum(clocks) / len(clocks), 1), "gfx_mhz_min": round(min(clocks), 1),
+           "gfx_mhz_max": round(max(clocks), 1), "samples": len(clocks),
+           "source": "amdsmi current GFX clock (mean of the XCDs), averaged over "
+                     f"{seconds:g} s of back-to-back launches after {settle:g} s of settling, "
+                     "after the timed region"}
+    if powers:
+        out["socket_power_w"] = round(sum(powers) / len(powers), 1)
+    return out
 
 
 def clock_fields(clock, achieved):

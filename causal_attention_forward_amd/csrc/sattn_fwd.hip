@@ -19,10 +19,10 @@
 //  * The K rows feeding S^T are permuted (the `krow` map below) so that the
 //    eight keys a lane holds for each 16-key slice of P^T are consecutive:
 //    the matching V^T operand is then one 16-byte LDS read.
-//  * A wave owns 32 query rows of one head.  A workgroup is NW = 8 waves (one
-//    per CU) or, when that would leave CUs idle, NW = 4 (two per CU); its
-//    waves are GW query heads of one GQA group times NW/GW row slots, so each
-//    K/V tile staged in LDS feeds all of them.  Query rows come in 32-row
+//  * A wave owns 32 query rows of one head.  A workgroup is eight waves (one
+//    per CU): GW query heads of one GQA group times 8/GW row slots, so each
+//    K/V tile staged in LDS feeds all of them.  Problems too small to give
+//    every CU such a workgroup go to the split-key kernel instead.  Query rows come in 32-row
 //    blocks; a slot takes block n-1-p (heavy) and then block p (light), so
 //    every workgroup carries the same causal work.
 //  * Each wave is software-pipelined: step j forms P V of tile j-1 and S of
@@ -31,10 +31,9 @@
 //    matrix products reads its LDS operand four products ahead and is
 //    followed by the exponentials of two scores.  Two register sets of S and
 //    of binary16 P alternate between steps, so no copies carry them.
-//  * K tile t is read at steps t-1 and t, V^T tile t at step t+1.  With one
-//    workgroup per CU (NW = 8) two K and two V^T tiles are staged per barrier,
-//    every other step, into rings of 6 and 5 LDS buffers (101 KiB); with two
-//    workgroups per CU (NW = 4) one of each per step, into rings of 4 and 3.
+//  * K tile t is read at steps t-1 and t, V^T tile t at step t+1.  Two K and
+//    two V^T tiles are staged per barrier, every other step, into rings of 6
+//    and 5 LDS buffers (101 KiB).
 //    Global loads run one stage (two steps) ahead of their LDS stores through
 //    registers, and every stage issues the same loads (tiles past the end
 //    read as zeros through buffer-descriptor range checks), so the waits on
@@ -85,6 +84,7 @@ constexpr float kLazy = 8.0f;                    // rescale threshold, base-2 un
 constexpr int kBufferWord3 = 0x00020000;         // raw buffer, 32-bit data format
 constexpr int kXcds = 8;                         // accelerator complex dies per MI355X
 constexpr int kCus = 256;                        // compute units per MI355X
+constexpr int kNW = 8;                           // waves per workgroup (one workgroup per CU)
 
 __device__ __forceinline__ half8 to_half8(float8v x) { return __builtin_convertvector(x, half8); }
 
@@ -160,18 +160,17 @@ __device__ __forceinline__ int vtr_offset(int lane, int mh, int hi) {
   return vchunk(row, col >> 3) + (col & 7);
 }
 
-template <int NW, int GW, bool VT_VEC, bool VROWS>
-__global__ void __launch_bounds__(64 * NW, 8 / NW)
+template <int GW, bool VT_VEC, bool VROWS>
+__global__ void __launch_bounds__(64 * kNW, 1)
 sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
                  const half_t* __restrict__ Vt, half_t* __restrict__ O, float* __restrict__ L,
                  float c, int T, int Hq, int Hkv, int G, int nBlocks, int nPairs, int nSlotGroups,
                  int nHeadGroups) {
-  constexpr int RS = NW / GW;              // row slots per workgroup
-  // With one workgroup per CU (NW = 8) two tiles are staged per barrier,
-  // which needs deeper rings (see the stage below).
-  constexpr bool kPair = NW == 8;
-  constexpr int kKRing = kPair ? 6 : 4;    // K tile t is read at steps t-1 and t
-  constexpr int kVRing = kPair ? 5 : 3;    // V^T tile t is read at step t+1
+  constexpr int RS = kNW / GW;             // row slots per workgroup
+  // Two tiles are staged per barrier, which needs these ring depths (see the
+  // stage below).
+  constexpr int kKRing = 6;                // K tile t is read at steps t-1 and t
+  constexpr int kVRing = 5;                // V^T tile t is read at step t+1
   constexpr float kSumCap = 256.0f;        // 2^kLazy
   constexpr int kOutOfRange = 0x7FFFFFF0;  // a buffer offset past every range
   __shared__ __attribute__((aligned(16))) half_t smem[(kKRing + kVRing) * kTileHalfs];
@@ -214,8 +213,8 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
   // Global -> register staging: thread t owns 16-byte chunk t of a K tile and
   // of a V^T tile (row cr, column chunk cc).  Two register sets, by stage
   // parity, keep loads two steps ahead of their LDS stores.
-  constexpr int kCpt = 8 / NW;          // 16-byte chunks per thread per tile
-  constexpr int kRowsPerPass = 8 * NW;  // tile rows one pass of the workgroup covers
+  constexpr int kCpt = 8 / kNW;          // 16-byte chunks per thread per tile
+  constexpr int kRowsPerPass = 8 * kNW;  // tile rows one pass of the workgroup covers
   const int cr = tid >> 3, cc = tid & 7;
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<half_t*>(K + (size_t)kv * T * kD), 0, T * kD * 2, kBufferWord3);
@@ -480,11 +479,7 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
     };
 
     // Ring schedule: K tile t is read at steps t-1 (S of t) and t (overflow
-    // fallback), V^T tile t at step t+1 (P V of t).  With NW = 4, stage j
-    // writes K of tile j+2 and V^T of tile j (loaded at stage j-2 into register
-    // set j % 2) into buffers last read at step j-2, then loads K of tile j+4
-    // and V^T of tile j+2 into the same set; one barrier per step.  With
-    // NW = 8, see the stage itself.
+    // fallback), V^T tile t at step t+1 (P V of t); see the stage itself.
     Stage setK[2], setV[2];
     {
       // every load of the prologue in flight before the first store waits
@@ -505,28 +500,21 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
     // has no branches.
     auto stage = [&](auto PARF, int j) {
       constexpr int P = decltype(PARF)::value;
-      if constexpr (kPair) {
-        // Even j only: K of tiles j+2, j+3 and V^T of tiles j, j+1 go into
-        // buffers whose tiles were last read at step j-3, before the previous
-        // barrier (j-2); other waves may still be in steps j-2, j-1, which read
-        // K of tiles j-2 .. j and V^T of tiles j-3, j-2 — other buffers.
-        if constexpr (P == 0) {
-          store_k((j + 2) % kKRing, setK[0]);
-          store_k((j + 3) % kKRing, setK[1]);
-          store_v(j % kVRing, setV[0]);
-          store_v((j + 1) % kVRing, setV[1]);
-          load_k(j + 4, setK[0]);
-          load_k(j + 5, setK[1]);
-          load_v(j + 2, setV[0]);
-          load_v(j + 3, setV[1]);
-          __builtin_amdgcn_s_waitcnt(0xC07F);
-          barrier();
-        }
-      } else {
-        store_k((j + 2) % kKRing, setK[P]);
-        store_v(j % kVRing, setV[P]);
-        load_k(j + 4, setK[P]);
-        load_v(j + 2, setV[P]);
+      // Even j only: K of tiles j+2, j+3 and V^T of tiles j, j+1 (loaded at
+      // stage j-2) go into buffers whose tiles were last read at step j-3,
+      // before the previous barrier (j-2); other waves may still be in steps
+      // j-2, j-1, which read K of tiles j-2 .. j and V^T of tiles j-3, j-2 —
+      // other buffers.  Then K of tiles j+4, j+5 and V^T of tiles j+2, j+3
+      // are loaded into the same registers.
+      if constexpr (P == 0) {
+        store_k((j + 2) % kKRing, setK[0]);
+        store_k((j + 3) % kKRing, setK[1]);
+        store_v(j % kVRing, setV[0]);
+        store_v((j + 1) % kVRing, setV[1]);
+        load_k(j + 4, setK[0]);
+        load_k(j + 5, setK[1]);
+        load_v(j + 2, setV[0]);
+        load_v(j + 3, setV[1]);
         __builtin_amdgcn_s_waitcnt(0xC07F);
         barrier();
       }
@@ -622,29 +610,21 @@ int check_device() {
   return ok ? SATTN_OK : SATTN_ERR_DEVICE;
 }
 
-template <int NW, int GW, bool VT_VEC, bool VROWS>
+// Eight-wave workgroups, one per CU; problems too small to give every CU one
+// go to the split-key kernel instead (see forward()).
+template <int GW, bool VT_VEC, bool VROWS>
 void launch(const half_t* Q, const half_t* K, const half_t* Vt, half_t* O, float* L, float c,
             int T, int Hq, int Hkv, hipStream_t stream) {
-  constexpr int RS = NW / GW;
+  constexpr int RS = kNW / GW;
   const int G = Hq / Hkv;
   const int nBlocks = (T + 31) / 32;
   const int nPairs = (nBlocks + 1) / 2;
   const int nSlotGroups = (nPairs + RS - 1) / RS;
   const int nHeadGroups = G / GW;
   const unsigned grid = (unsigned)nSlotGroups * (unsigned)Hkv * (unsigned)nHeadGroups;
-  hipLaunchKernelGGL((sattn_fwd_kernel<NW, GW, VT_VEC, VROWS>), dim3(grid), dim3(64 * NW), 0,
+  hipLaunchKernelGGL((sattn_fwd_kernel<GW, VT_VEC, VROWS>), dim3(grid), dim3(64 * kNW), 0,
                      stream, Q, K, Vt, O, L, c, T, Hq, Hkv, G, nBlocks, nPairs, nSlotGroups,
                      nHeadGroups);
-}
-
-// Eight-wave workgroups (one per CU); problems too small to give every CU
-// one go to the split-key kernel instead (see forward()).  The kernel also
-// builds for four-wave workgroups (two per CU), which measured slower than
-// the split-key kernel wherever eight-wave ones cannot fill the chip.
-template <int GW, bool VT_VEC, bool VROWS>
-void launch_nw(const half_t* Q, const half_t* K, const half_t* Vt, half_t* O, float* L, float c,
-               int T, int Hq, int Hkv, hipStream_t stream) {
-  launch<8, GW, VT_VEC, VROWS>(Q, K, Vt, O, L, c, T, Hq, Hkv, stream);
 }
 
 // V^T chunks of 8 keys are whole 16-byte loads only when T % 8 == 0; V rows
@@ -653,11 +633,11 @@ template <int GW, bool VROWS>
 void launch_gw(const half_t* Q, const half_t* K, const half_t* V, half_t* O, float* L, float c,
                int T, int Hq, int Hkv, hipStream_t stream) {
   if (VROWS)
-    launch_nw<GW, false, true>(Q, K, V, O, L, c, T, Hq, Hkv, stream);
+    launch<GW, false, true>(Q, K, V, O, L, c, T, Hq, Hkv, stream);
   else if (T % 8 == 0)
-    launch_nw<GW, true, false>(Q, K, V, O, L, c, T, Hq, Hkv, stream);
+    launch<GW, true, false>(Q, K, V, O, L, c, T, Hq, Hkv, stream);
   else
-    launch_nw<GW, false, false>(Q, K, V, O, L, c, T, Hq, Hkv, stream);
+    launch<GW, false, false>(Q, K, V, O, L, c, T, Hq, Hkv, stream);
 }
 
 template <bool VROWS>
