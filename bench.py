@@ -395,6 +395,40 @@ def compulsory_bytes(T, Hq, Hkv, d=64):
     return 2 * d * T * (Hq + 2 * Hkv) + 2 * d * T * Hq + 4 * T * Hq
 
 
+def graph_time(torch, call, calls, reps, outputs):
+    """Median per-call time of `calls` launches captured once in a HIP graph
+    and replayed (the device's own back-to-back time, without the host's
+    per-call launch cost), and whether the tensors in `outputs` hold, after
+    the replays, exactly what they held before the capture (the same
+    deterministic result as the eager calls).  The captured work is the
+    library's kernel launches only.  (None, None) if the capture fails."""
+    import statistics
+    before = [t.clone() for t in outputs]
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            sp = torch.cuda.current_stream().cuda_stream
+            for i in range(calls):
+                call(i, sp)
+    except Exception:
+        return None, None
+    stream = torch.cuda.current_stream()
+    g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        times.append(ev0.elapsed_time(ev1) / calls)
+    same = all(torch.equal(a, b) for a, b in zip(before, outputs))
+    del g
+    return statistics.median(times), same
+
+
 def sweep(torch, sattn, workloads, make_workload, reps=5, calls=50):
     """Every synthetic workload: median over `reps` runs of `calls` back-to-back
     launches, cycling through enough input/output sets (at least 4, about
@@ -414,9 +448,11 @@ def sweep(torch, sattn, workloads, make_workload, reps=5, calls=50):
                          torch.empty((x.T, x.Hq * 64), dtype=torch.float16, device=dev),
                          torch.empty((x.Hq, x.T), dtype=torch.float32, device=dev)))
 
-        def call(i):
+        def call(i, sp=stream.cuda_stream):
             q, k, vt, O, L = sets[i % nsets]
-            sattn.fwd(q, k, vt, x.c, out=O, lse=L, stream=stream)
+            st = sattn.sattn_fwd(q.data_ptr(), k.data_ptr(), vt.data_ptr(), O.data_ptr(),
+                                 L.data_ptr(), x.c, x.T, x.Hq, x.Hkv, sp)
+            assert st == sattn.SATTN_OK, st
 
         for i in range(max(200, 2 * nsets)):
             call(i)
@@ -432,12 +468,19 @@ def sweep(torch, sattn, workloads, make_workload, reps=5, calls=50):
             torch.cuda.synchronize()
             times.append(ev0.elapsed_time(ev1) / calls)
         ms = statistics.median(times)
+        gms, same = graph_time(torch, call, calls, reps, sets[0][3:5])
         tflops = causal_flops(x.T, x.Hq) / (ms * 1e-3) / 1e12
-        print(json.dumps({
-            "sweep": w.name, "T": x.T, "Hq": x.Hq, "Hkv": x.Hkv, "us_per_call": round(ms * 1e3, 2),
-            "tflops": round(tflops, 2), "pct_fp16_peak": round(100 * tflops / PEAK_FP16_TFLOPS, 2),
-            "compulsory_bytes": nbytes, "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-            "input_sets": nsets}), flush=True)
+        out = {"sweep": w.name, "T": x.T, "Hq": x.Hq, "Hkv": x.Hkv,
+               "us_per_call": round(ms * 1e3, 2), "tflops": round(tflops, 2),
+               "pct_fp16_peak": round(100 * tflops / PEAK_FP16_TFLOPS, 2),
+               "compulsory_bytes": nbytes, "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+               "input_sets": nsets}
+        if gms is not None:
+            gtf = causal_flops(x.T, x.Hq) / (gms * 1e-3) / 1e12
+            out.update({"graph_us_per_call": round(gms * 1e3, 2), "graph_tflops": round(gtf, 2),
+                        "graph_gbps": round(nbytes / (gms * 1e-3) / 1e9, 1),
+                        "graph_matches_eager": same})
+        print(json.dumps(out), flush=True)
         del sets
         torch.cuda.empty_cache()
 
@@ -470,7 +513,7 @@ def sweep_backward(torch, sattn, workloads, make_workload, reps=5, calls=20):
                          torch.empty((Hq, T, 64), **f32), torch.empty((Hkv, T, 64), **f32),
                          torch.empty((Hkv, 64, T), **f32), torch.empty((Hq, T), **f32)))
 
-        def call(i):
+        def call(i, sp=sp):
             q, k, vt, O, g, L, dQ, dK, dVt, D = sets[i % nsets]
             st = sattn.sattn_bwd(q.data_ptr(), k.data_ptr(), vt.data_ptr(), O.data_ptr(),
                                  g.data_ptr(), L.data_ptr(), dQ.data_ptr(), dK.data_ptr(),
@@ -492,13 +535,21 @@ def sweep_backward(torch, sattn, workloads, make_workload, reps=5, calls=20):
             torch.cuda.synchronize()
             times.append(ev0.elapsed_time(ev1) / calls)
         ms = statistics.median(times)
+        # with GQA the grouped planes live in the shared workspace, so the
+        # replay check covers one set's dQ, dK, dV^T and D
+        gms, same = graph_time(torch, call, calls, reps, sets[0][6:10] if nsets > 1 else ())
         tflops = backward_flops(T, Hq) / (ms * 1e-3) / 1e12
-        print(json.dumps({
-            "sweep_backward": w.name, "T": T, "Hq": Hq, "Hkv": Hkv,
-            "us_per_call": round(ms * 1e3, 2), "tflops_algorithmic": round(tflops, 2),
-            "pct_fp16_peak": round(100 * tflops / PEAK_FP16_TFLOPS, 2),
-            "compulsory_bytes": nbytes, "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-            "input_sets": nsets}), flush=True)
+        out = {"sweep_backward": w.name, "T": T, "Hq": Hq, "Hkv": Hkv,
+               "us_per_call": round(ms * 1e3, 2), "tflops_algorithmic": round(tflops, 2),
+               "pct_fp16_peak": round(100 * tflops / PEAK_FP16_TFLOPS, 2),
+               "compulsory_bytes": nbytes, "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+               "input_sets": nsets}
+        if gms is not None:
+            gtf = backward_flops(T, Hq) / (gms * 1e-3) / 1e12
+            out.update({"graph_us_per_call": round(gms * 1e3, 2),
+                        "graph_tflops_algorithmic": round(gtf, 2),
+                        "graph_matches_eager": same if nsets > 1 else None})
+        print(json.dumps(out), flush=True)
         del sets, ws
         torch.cuda.empty_cache()
 
