@@ -51,20 +51,20 @@
 #include <atomic>
 
 #include "sattn.h"
+#include "sattn_lds.h"
 
 namespace {
 
 typedef _Float16 half_t;
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 typedef int int4v __attribute__((ext_vector_type(4)));
 
 constexpr int kD = SATTN_HEAD_DIM;              // head width
 constexpr int kTile = 64;                       // rows of a staged K, V^T, Q or dO tile
-constexpr int kRowHalfs = kD;                   // LDS row: 64 values, 16-byte chunks swizzled
+constexpr int kRowHalfs = sattn_lds::kRowHalfs; // LDS row: 64 values, 16-byte chunks swizzled
 constexpr int kTileHalfs = kTile * kRowHalfs;
 constexpr int kBufferWord3 = 0x00020000;        // raw buffer, 32-bit data format
 constexpr int kOutOfRange = 0x7FFFFFF0;         // a buffer offset past every range
@@ -104,51 +104,9 @@ __device__ __forceinline__ half8 ld8(const half_t* p) { return *reinterpret_cast
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 constexpr int kLdsDone = 0xC07F;  // s_waitcnt lgkmcnt(0), other counters unconstrained
 
-// ds_read_b64_tr_b16 at p: within each 16-lane group, lane 4a + b supplies
-// the address of row a, columns 4b'..4b'+3 of a block, and lane t receives
-// rows 0..3 of the column that lanes 4(t/4)'s supplier pointed at, offset t%4.
-__device__ __forceinline__ half4 lds_tr4(const half_t* p) {
-  typedef __attribute__((address_space(3))) short4v lds_short4;
-  const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(const_cast<half_t*>(p)));
-  return __builtin_bit_cast(half4, v);
-}
-
-// LDS tiles keep 64-value rows unpadded and place 16-byte chunk c of row r at
-// chunk c ^ swz(r), swz(r) = the three bits of (r/2) % 8 reversed.  Sixteen
-// lanes reading one chunk of 16 consecutive rows (the natural operand read)
-// then hit all 64 banks once, and so do 32 lanes of a transpose read (four
-// rows, four chunks each): rows r and r+2 land in opposite halves of the row
-// and odd rows in the other 32 banks.  The pad of the forward's tiles cannot do
-// both.  swz depends on r only through (r/2) % 8, so an offset of 16 rows
-// keeps it.
-__device__ __forceinline__ int swz(int r) {
-  const int v = (r >> 1) & 7;
-  return ((v & 1) << 2) | (v & 2) | (v >> 2);
-}
-
-// Offset (halfs) of 16-byte chunk c of row r in a swizzled tile.
-__device__ __forceinline__ int chunk_offset(int r, int c) { return r * kRowHalfs + ((c ^ swz(r)) << 3); }
-
-// Operand whose lane l holds X[m][k0 + 8(l/32) .. +7] for a tile stored
-// k-major in LDS (X[m][k] at row k, column m): two transpose reads, rows
-// k .. k+3 at lo and k+4 .. k+7 at hi (offsets include the lane's own part).
-__device__ __forceinline__ half8 tr8(const half_t* base, int lo, int hi) {
-  const half4 a = lds_tr4(base + lo), b = lds_tr4(base + hi);
-  return half8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-// A lane's tr8 offset (halfs) over a k-major tile for operand rows m in
-// 32 mh .. 32 mh + 31 and the read of rows 4 hi .. (hi = 0, 1): row
-// 8(l/32) + (l%16)/4 + 4 hi, column 32 mh + 16((l/16)%2) + 4 c(l%4), where c
-// is the identity (the operand's row m is l%32) or swaps the two bits of l%4
-// (its row m is krow(l%32)).
-__device__ __forceinline__ int tr_offset(int lane, bool permuted, int mh, int hi) {
-  const int b = lane & 3;
-  const int cb = permuted ? (((b & 1) << 1) | (b >> 1)) : b;
-  const int row = 8 * (lane >> 5) + ((lane & 15) >> 2) + 4 * hi;
-  const int col = 32 * mh + 16 * ((lane >> 4) & 1) + 4 * cb;
-  return chunk_offset(row, col >> 3) + (col & 7);
-}
+using sattn_lds::chunk_offset;
+using sattn_lds::tr8;
+using sattn_lds::tr_offset;
 
 // binary16 operand of 16 consecutive indices from accumulator elements
 // 8h .. 8h+7 (round to nearest even).

@@ -16,16 +16,21 @@
 //  * Workgroup = four waves on one 32-row query block of one head; wave w
 //    takes key tiles w, w + 4, w + 8, ... up to the block's diagonal, so a
 //    block's key range is walked four times faster than by one wave.
-//  * No LDS staging and no barrier in the loop: a wave reads its K rows and
-//    V^T rows straight from global memory (L2) as 16-byte operand loads, the
-//    next tile's loads in flight while the current tile is computed.  Given V
-//    as rows, the V^T operand is gathered with 2-byte loads (lanes of a load
-//    hold consecutive d, so each load still reads whole row segments).
+//  * Each wave stages its own tiles in a private LDS region, so the loop
+//    has no barrier: a tile's K rows and V^T rows (or V rows) are read with
+//    fully coalesced 16-byte loads (eight whole 128-byte lines per
+//    instruction; rows and keys past T read as zeros through the buffer
+//    range checks), the next tile's loads in flight while the current one is
+//    computed, and stored swizzled so that the operand reads hit every bank
+//    once.  Given V as rows, the V^T operand comes from transpose reads of
+//    the V-rows tile.  (Operands loaded straight from global memory, as
+//    16-byte pieces of 32 different lines per instruction, left the CU's
+//    load path the bottleneck.)
 //  * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_f16 (a lane owns one
 //    query and 16 keys, so a row's max and sum are in-lane plus one exchange
 //    with the lane 32 away); K rows are permuted so each lane's 8 keys per
 //    16-key slice of P^T are consecutive (one 16-byte V^T read per operand).
-//  * The merge: waves 1..3 leave m, l and O^T in LDS; wave 0 forms
+//  * The merge: waves 1..3 leave m, l and O^T in their LDS regions; wave 0 forms
 //    M = max m_w, l = sum l_w 2^(m_w - M), O = sum O_w 2^(m_w - M) and writes
 //    O / l and M + log2 l.
 #include <hip/hip_runtime.h>
@@ -34,6 +39,7 @@
 
 #include "sattn.h"
 #include "sattn_internal.h"
+#include "sattn_lds.h"
 
 namespace {
 
@@ -42,10 +48,19 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef float float16v __attribute__((ext_vector_type(16)));
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+using sattn_lds::chunk_offset;
+using sattn_lds::tr8;
+using sattn_lds::tr_offset;
 
 constexpr int kD = SATTN_HEAD_DIM;
 constexpr int kWaves = 4;
 constexpr int kXcds = 8;
+constexpr int kTileHalfs = 64 * sattn_lds::kRowHalfs;  // one staged 64 x 64 tile
+constexpr int kBufferWord3 = 0x00020000;               // raw buffer, 32-bit data format
+constexpr int kOutOfRange = 0x7FFFFFF0;                // a buffer offset past every range
+constexpr int kLdsDone = 0xC07F;                       // s_waitcnt lgkmcnt(0) only
 
 __device__ __forceinline__ float16v mfma(half8 a, half8 b, float16v c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -64,18 +79,14 @@ __device__ __forceinline__ int krow(int m) {
 
 __device__ __forceinline__ half8 ld8(const half_t* p) { return *reinterpret_cast<const half8*>(p); }
 
-struct Tile {
-  half8 k[8];  // K operand: key rows krow(n) (+32), d = 16 kk + 8g ..    (index 2 kk + half)
-  half8 v[8];  // V^T operand: d rows n (+32), keys 16 ks + 8g ..          (index 2 ks + half)
-};
-
 template <bool VT_VEC, bool VROWS>
 __global__ void __launch_bounds__(64 * kWaves, 2)
 sattn_fwd_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
                        const half_t* __restrict__ Vt, half_t* __restrict__ O,
                        float* __restrict__ L, float c, int T, int Hq, int G, int nBlocks) {
-  __shared__ float xo[kWaves - 1][2][16][64];  // waves 1..3: O^T accumulators, lane-major
-  __shared__ float xm[kWaves - 1][64], xl[kWaves - 1][64];
+  // wave w's region: its K tile and its V^T (or V-rows) tile; after the key
+  // loop, for w > 0, its partial (O^T, m, l) for the merge
+  __shared__ __attribute__((aligned(16))) half_t region[kWaves][2 * kTileHalfs];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -100,53 +111,83 @@ sattn_fwd_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ 
   for (int kk = 0; kk < 4; ++kk)
     qf[kk] = row < T ? ld8(Q + ((size_t)h * T + row) * kD + 16 * kk + 8 * g) : half8{};
 
-  const half_t* Kh = K + (size_t)kv * T * kD;
-  const half_t* Vh = Vt + (size_t)kv * kD * T;
-  auto load = [&](int kt, Tile& t) {
+  // Staging: lane l owns 16-byte chunk l + 64 i (i < 8) of each tile: row
+  // l/8 + 8i, chunk l%8.  K (and V rows) tiles are 8 KiB contiguous; a V^T
+  // tile is 64 rows of 128 bytes, T values apart.
+  half_t* const ktile = region[wave];
+  half_t* const vtile = region[wave] + kTileHalfs;
+  const int sr = lane >> 3, sc = lane & 7;
+  const half_t* Vh = Vt + (size_t)kv * kD * T;  // V^T of head kv, or (VROWS) its V rows
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<half_t*>(K + (size_t)kv * T * kD), 0, T * kD * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(Vh), 0, kD * T * 2, kBufferWord3);
+  int4v st[16];  // the next tile: K chunks 0..7, V chunks 8..15
+  auto load = [&](int kt) {
     const int key0 = kt * 64;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int i = 0; i < 8; ++i) {
+      const int r = sr + 8 * i;
+      st[i] = __builtin_amdgcn_raw_buffer_load_b128(krsrc, ((key0 + r) * kD + sc * 8) * 2, 0, 0);
+      if (VROWS) {  // rows past T read as zeros, like K's
+        st[8 + i] = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, ((key0 + r) * kD + sc * 8) * 2, 0, 0);
+      } else if (VT_VEC) {  // T % 8 == 0: a chunk lies wholly before or past T
+        const int off = key0 + sc * 8 < T ? (r * T + key0 + sc * 8) * 2 : kOutOfRange;
+        st[8 + i] = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off, 0, 0);
+      } else {
+        const int k0 = key0 + sc * 8;
+        half8 x;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int key = key0 + 32 * hf + krow(n);
-        t.k[2 * kk + hf] = key < T ? ld8(Kh + (size_t)key * kD + 16 * kk + 8 * g) : half8{};
+        for (int e = 0; e < 8; ++e) x[e] = k0 + e < T ? Vh[(size_t)r * T + k0 + e] : (half_t)0;
+        st[8 + i] = __builtin_bit_cast(int4v, x);
       }
+    }
+  };
+  auto store = [&]() {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int i = 0; i < 8; ++i) {
+      const int off = chunk_offset(sr + 8 * i, sc);
+      *reinterpret_cast<int4v*>(ktile + off) = st[i];
+      *reinterpret_cast<int4v*>(vtile + off) = st[8 + i];
+    }
+  };
+  // Operand reads: K rows krow(n) (+32) and V^T rows n (+32), chunk 2j + g;
+  // with V rows, transpose reads of keys 16 ks .. of the V-rows tile.
+  int kOff[4], vOff[4];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int d = 32 * hf + n, k0 = key0 + 16 * ks + 8 * g;
-        const half_t* src = Vh + (size_t)d * T + k0;
-        if (VROWS) {  // V rows [T][64]: element (key, d) at key * 64 + d
-          half8 x;
+  for (int j = 0; j < 4; ++j) {
+    kOff[j] = chunk_offset(krow(n), 2 * j + g);
+    vOff[j] = chunk_offset(n, 2 * j + g);
+  }
+  int tOff[2][2];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = k0 + e < T ? Vh[(size_t)(k0 + e) * kD + d] : (half_t)0;
-          t.v[2 * ks + hf] = x;
-        } else if (VT_VEC && k0 + 7 < T) {
-          t.v[2 * ks + hf] = ld8(src);
-        } else {
-          half8 x;
+  for (int mh = 0; mh < 2; ++mh)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = k0 + e < T ? src[e] : (half_t)0;
-          t.v[2 * ks + hf] = x;
-        }
-      }
+    for (int hi = 0; hi < 2; ++hi) tOff[mh][hi] = VROWS ? tr_offset(lane, false, mh, hi) : 0;
+  auto vt_operand = [&](int ks, int hf) -> half8 {
+    if constexpr (VROWS)
+      return tr8(vtile + 16 * ks * sattn_lds::kRowHalfs, tOff[hf][0], tOff[hf][1]);
+    else
+      return ld8(vtile + vOff[ks] + 32 * hf * sattn_lds::kRowHalfs);
   };
 
   float m = -INFINITY, l = 0.0f;
   float16v o0 = {}, o1 = {};
   const int swapAddr = (lane ^ 32) << 2;
-  Tile cur, nxt;
   int kt = wave;
-  if (kt < need) load(kt, cur);
+  if (kt < need) load(kt);
   while (kt < need) {
+    // this wave's own region: its reads of the previous tile were consumed
+    // by the products, so the stores may overwrite it
+    store();
+    __builtin_amdgcn_s_waitcnt(kLdsDone);
     const int kn = kt + kWaves;
-    if (kn < need) load(kn, nxt);
+    if (kn < need) load(kn);
     float16v s0 = {}, s1 = {};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      s0 = mfma(cur.k[2 * kk], qf[kk], s0);
-      s1 = mfma(cur.k[2 * kk + 1], qf[kk], s1);
+      s0 = mfma(ld8(ktile + kOff[kk]), qf[kk], s0);
+      s1 = mfma(ld8(ktile + kOff[kk] + 32 * sattn_lds::kRowHalfs), qf[kk], s1);
     }
     if (kt == need - 1) {  // the tile crossing the block's diagonal
       const int lim = row - kt * 64 - 8 * g;
@@ -184,43 +225,43 @@ sattn_fwd_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ 
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      o0 = mfma(cur.v[2 * ks], p[ks], o0);
-      o1 = mfma(cur.v[2 * ks + 1], p[ks], o1);
+      o0 = mfma(vt_operand(ks, 0), p[ks], o0);
+      o1 = mfma(vt_operand(ks, 1), p[ks], o1);
     }
-    if (kn < need) cur = nxt;
     kt = kn;
   }
 
   // merge the four waves' (m, l, O) of the same 32 rows; l is a partial sum
   // per lane (keys of its half), so the pair's sums are added first
   l += xlane(l, swapAddr);
+  float* const part = reinterpret_cast<float*>(region[wave]);  // [2][16][64] O^T, [64] m, [64] l
   if (wave > 0) {
-    const int w = wave - 1;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      xo[w][0][i][lane] = o0[i];
-      xo[w][1][i][lane] = o1[i];
+      part[i * 64 + lane] = o0[i];
+      part[(16 + i) * 64 + lane] = o1[i];
     }
-    xm[w][lane] = m;
-    xl[w][lane] = l;
+    part[32 * 64 + lane] = m;
+    part[33 * 64 + lane] = l;
   }
   __syncthreads();
   if (wave != 0) return;
   float M = m;
 #pragma unroll
-  for (int w = 0; w < kWaves - 1; ++w) M = fmaxf(M, xm[w][lane]);
+  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, reinterpret_cast<const float*>(region[w])[32 * 64 + lane]);
   const float a0 = __builtin_amdgcn_exp2f(m - M);
   float lt = l * a0;
   o0 *= a0;
   o1 *= a0;
 #pragma unroll
-  for (int w = 0; w < kWaves - 1; ++w) {
-    const float aw = __builtin_amdgcn_exp2f(xm[w][lane] - M);  // 0 for a wave with no tile
-    lt += xl[w][lane] * aw;
+  for (int w = 1; w < kWaves; ++w) {
+    const float* pw = reinterpret_cast<const float*>(region[w]);
+    const float aw = __builtin_amdgcn_exp2f(pw[32 * 64 + lane] - M);  // 0 for a wave with no tile
+    lt += pw[33 * 64 + lane] * aw;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      o0[i] += xo[w][0][i][lane] * aw;
-      o1[i] += xo[w][1][i][lane] * aw;
+      o0[i] += pw[i * 64 + lane] * aw;
+      o1[i] += pw[(16 + i) * 64 + lane] * aw;
     }
   }
   if (row < T) {
