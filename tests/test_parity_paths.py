@@ -1,5 +1,6 @@
-"""Parity on inputs built to drive the kernel's less common paths, on both
-workgroup shapes (eight waves when the grid fills every CU, four otherwise).
+"""Parity on inputs built to drive the kernels' less common paths, on both
+kernels (the eight-wave main kernel when its grid fills every CU, the
+split-key kernel otherwise).
 
 * Rising scores: keys carry a ramp along the sequence, so a row's running
   maximum grows by several base-2 units per 64-key tile and the reference
@@ -21,7 +22,7 @@ from parity_util import TOL_L, TOL_O, assert_close, note, run, sample_rows
 
 pytestmark = pytest.mark.gpu
 
-# (T, Hq, Hkv): the first is a four-wave grid, the second an eight-wave one
+# (T, Hq, Hkv): the first takes the split-key kernel, the second the main kernel
 PATH_SHAPES = [(1000, 8, 2), (4096, 32, 8)]
 
 
@@ -94,3 +95,14 @@ def test_eight_wave_shapes(sattn, dev, shape):
     note(f"eight-wave grid T={T} Hq={hq} Hkv={hkv}")
     x = make_inputs(T, hq, hkv, seed=23, peaked_fraction=0.01)
     compare(sattn, dev, x, f"T={T} Hq={hq} Hkv={hkv}")
+
+
+@pytest.mark.parametrize("shape", [(8191, 2, 1), (8192, 4, 2)])
+def test_split_key_long_sequences(sattn, dev, shape):
+    """Grids too small for the main kernel at long T: each wave of the
+    split-key kernel walks up to 32 key tiles through its own LDS region and
+    the four partials are merged; T % 8 != 0 takes the scalar V^T staging."""
+    T, hq, hkv = shape
+    note(f"split-key kernel, long sequence T={T} Hq={hq} Hkv={hkv}")
+    x = make_inputs(T, hq, hkv, seed=24, qk_std=1.25)
+    compare(sattn, dev, x, f"split-key T={T} Hq={hq} Hkv={hkv}")

@@ -26,7 +26,7 @@ def both(sattn, dev, x):
 
 
 SHAPES = [(1, 1, 1), (7, 2, 1), (64, 4, 2), (100, 3, 3), (257, 6, 2), (1000, 16, 4),
-          (1023, 8, 8), (4095, 32, 8), (8192, 16, 16)]
+          (1023, 8, 8), (4095, 32, 8), (8192, 16, 16), (8192, 4, 2)]
 
 
 @pytest.mark.parametrize("T,Hq,Hkv", SHAPES, ids=[f"T{t}_Hq{a}_Hkv{b}" for t, a, b in SHAPES])
