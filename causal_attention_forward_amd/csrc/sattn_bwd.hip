@@ -532,6 +532,387 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
 }
 
 // -------------------------------------------------------------------------
+// Launches for grids too small to fill the chip: a workgroup of four waves
+// takes one 32-row block (queries, or keys) of one head and its waves walk
+// the block's tiles round-robin (tile w, w + 4, ...), each staging its own
+// tiles in a private LDS region (coalesced loads, no barrier in the loop).
+// The four partial accumulators are summed in wave order at the end, so the
+// result is deterministic.  The tile bodies are those of the launches above.
+// -------------------------------------------------------------------------
+constexpr int kSW = 4;  // waves per workgroup of the split launches
+
+template <bool VT_VEC, bool PREFETCH>
+__global__ void __launch_bounds__(64 * kSW, 2)
+sattn_bwdq_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
+                        const half_t* __restrict__ Vt, const half_t* __restrict__ O,
+                        const half_t* __restrict__ dO, const float* __restrict__ L,
+                        float* __restrict__ dQ, float* __restrict__ D, float c, float s, int T,
+                        int Hq, int G, int nBlocks) {
+  // wave w's region: its K tile and V^T tile; afterwards (w > 0) its partial dQ
+  __shared__ __attribute__((aligned(16))) half_t region[kSW][2 * kTileHalfs];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 31;
+  const int g = lane >> 5;
+
+  // K/V head first, then query blocks heaviest first, then the group's heads
+  const int lid = xcd_order();
+  const int kv = lid / (nBlocks * G);
+  const int rem = lid - kv * nBlocks * G;
+  const int blk = nBlocks - 1 - rem / G;
+  const int h = kv * G + rem % G;
+  const int row0 = 32 * blk;
+  const int row = row0 + n;
+  const bool live = row < T;
+  const int nkt = min(T - 1, row0 + 31) / kTile + 1;  // key tiles up to the diagonal
+
+  half8 qf[4], dof[4];
+  float dpart = 0.0f;
+  {
+    const half_t* qrow = Q + ((size_t)h * T + row) * kD + 8 * g;
+    const size_t tok = (size_t)row * Hq * kD + (size_t)h * kD + 8 * g;
+  #pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const half8 z = {};
+      qf[kk] = live ? ld8(qrow + 16 * kk) : z;
+      dof[kk] = live ? *reinterpret_cast<const half8*>(dO + tok + 16 * kk) : z;
+      const half8 of = live ? *reinterpret_cast<const half8*>(O + tok + 16 * kk) : z;
+  #pragma unroll
+      for (int e = 0; e < 8; ++e) dpart = fmaf((float)dof[kk][e], (float)of[e], dpart);
+    }
+  }
+  const float Drow = dpart + xlane(dpart, (lane ^ 32) << 2);
+  const float negL = live ? -L[(size_t)h * T + row] : 0.0f;
+  float16v negD;
+  #pragma unroll
+  for (int i = 0; i < 16; ++i) negD[i] = -Drow;
+  if (wave == 0 && live && g == 0) D[(size_t)h * T + row] = Drow;
+
+  // Staging: lane l owns chunk l + 64 i (i < 8) of each tile: row l/8 + 8i,
+  // chunk l%8 (tiles past the end and V^T chunks past T read as zeros).
+  half_t* const kb = region[wave];
+  half_t* const vb = region[wave] + kTileHalfs;
+  const int sr = lane >> 3, sc = lane & 7;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<half_t*>(K + (size_t)kv * T * kD), 0, T * kD * 2, kBufferWord3);
+  const half_t* Vh = Vt + (size_t)kv * kD * T;
+  const __amdgpu_buffer_rsrc_t vrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(Vh), 0, kD * T * 2, kBufferWord3);
+  int4v st[16];  // the next tile: K chunks 0..7, V^T chunks 8..15
+  auto load = [&](int kt) {
+    const int key0 = kt * kTile;
+  #pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = sr + 8 * i;
+      st[i] = __builtin_amdgcn_raw_buffer_load_b128(krsrc, ((key0 + r) * kD + sc * 8) * 2, 0, 0);
+      if (VT_VEC) {
+        const int off = key0 + sc * 8 < T ? (r * T + key0 + sc * 8) * 2 : kOutOfRange;
+        st[8 + i] = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off, 0, 0);
+      } else {
+        half8 v;
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = key0 + sc * 8 + e;
+          v[e] = key < T ? Vh[(size_t)r * T + key] : (half_t)0;
+        }
+        st[8 + i] = __builtin_bit_cast(int4v, v);
+      }
+    }
+  };
+  auto store = [&]() {
+  #pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int off = chunk_offset(sr + 8 * i, sc);
+      *reinterpret_cast<int4v*>(kb + off) = st[i];
+      *reinterpret_cast<int4v*>(vb + off) = st[8 + i];
+    }
+  };
+
+  int kOff[4];
+  #pragma unroll
+  for (int kk = 0; kk < 4; ++kk) kOff[kk] = chunk_offset(krow(n), 2 * kk + g);
+  int vtOff[2][2], ktOff[2][2];
+  #pragma unroll
+  for (int mh = 0; mh < 2; ++mh)
+  #pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      vtOff[mh][hi] = tr_offset(lane, true, mh, hi);
+      ktOff[mh][hi] = tr_offset(lane, false, mh, hi);
+    }
+
+  float16v dq0 = {}, dq1 = {};
+  int kt = wave;
+  if (PREFETCH && kt < nkt) load(kt);
+  while (kt < nkt) {
+    // the previous tile's reads were consumed by the products
+    if (!PREFETCH) load(kt);
+    store();
+    __builtin_amdgcn_s_waitcnt(kLdsDone);
+    const int kn = kt + kSW;
+    if (PREFETCH && kn < nkt) load(kn);
+    float16v s0, s1, p0, p1;
+  #pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      s0 = mfma(ld8(kb + kOff[kk]), qf[kk], kk == 0 ? float16v{} : s0);
+      s1 = mfma(ld8(kb + kOff[kk] + 32 * kRowHalfs), qf[kk], kk == 0 ? float16v{} : s1);
+      const half_t* vk = vb + 16 * kk * kRowHalfs;
+      p0 = mfma(tr8(vk, vtOff[0][0], vtOff[0][1]), dof[kk], kk == 0 ? negD : p0);
+      p1 = mfma(tr8(vk, vtOff[1][0], vtOff[1][1]), dof[kk], kk == 0 ? negD : p1);
+    }
+    if (kt * kTile + kTile - 1 > row0) {
+      const int lim = row - kt * kTile - 8 * g;
+  #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int k = 16 * (i >> 3) + (i & 7);
+        if (k > lim) s0[i] = -INFINITY;
+        if (k + 32 > lim) s1[i] = -INFINITY;
+      }
+    }
+  #pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c, negL)) * p0[i];
+      s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c, negL)) * p1[i];
+    }
+    const half8 ds[4] = {pack8(s0, 0), pack8(s0, 1), pack8(s1, 0), pack8(s1, 1)};
+  #pragma unroll
+    for (int ck = 0; ck < 4; ++ck) {
+      const half_t* kc = kb + 16 * ck * kRowHalfs;
+      dq0 = mfma(tr8(kc, ktOff[0][0], ktOff[0][1]), ds[ck], dq0);
+      dq1 = mfma(tr8(kc, ktOff[1][0], ktOff[1][1]), ds[ck], dq1);
+    }
+    kt = kn;
+  }
+
+  // sum the four partials in wave order
+  float* const part = reinterpret_cast<float*>(region[wave]);
+  if (wave > 0) {
+  #pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      part[i * 64 + lane] = dq0[i];
+      part[(16 + i) * 64 + lane] = dq1[i];
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  #pragma unroll
+  for (int w = 1; w < kSW; ++w) {
+    const float* pw = reinterpret_cast<const float*>(region[w]);
+  #pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dq0[i] += pw[i * 64 + lane];
+      dq1[i] += pw[(16 + i) * 64 + lane];
+    }
+  }
+  if (live) {
+    float* out = dQ + ((size_t)h * T + row) * kD + 4 * g;
+  #pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4v a = {dq0[4 * q], dq0[4 * q + 1], dq0[4 * q + 2], dq0[4 * q + 3]};
+      const float4v b = {dq1[4 * q], dq1[4 * q + 1], dq1[4 * q + 2], dq1[4 * q + 3]};
+      *reinterpret_cast<float4v*>(out + 8 * q) = a * s;
+      *reinterpret_cast<float4v*>(out + 32 + 8 * q) = b * s;
+    }
+  }
+}
+
+template <bool PREFETCH>
+__global__ void __launch_bounds__(64 * kSW, 2)
+sattn_bwdk_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
+                        const half_t* __restrict__ Vt, const half_t* __restrict__ dO,
+                        const float* __restrict__ L, const float* __restrict__ D,
+                        float* __restrict__ dKp, float* __restrict__ dVp, float c, float s, int T,
+                        int Hq, int G, int nBlocks) {
+  // wave w's region: its Q tile, dO tile and the tile's L and -D; afterwards
+  // (w > 0) its partial dK^T and dV^T
+  constexpr int kRegion = 2 * kTileHalfs * 2 + 2 * kTile * 4;  // bytes
+  __shared__ __attribute__((aligned(16))) char region[kSW][kRegion];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 31;
+  const int g = lane >> 5;
+
+  // K/V head first, then key blocks heaviest (first) first, then the group's heads
+  const int lid = xcd_order();
+  const int kv = lid / (nBlocks * G);
+  const int rem = lid - kv * nBlocks * G;
+  const int blk = rem / G;
+  const int h = kv * G + rem % G;
+  const int key0 = 32 * blk;
+  const int key = key0 + n;
+  const bool live = key < T;
+  const int ft = key0 / kTile;  // the first query tile holding a query >= key0
+  const int nt = (T + kTile - 1) / kTile;
+
+  half8 kf[4], vf[4];
+  {
+    const half_t* krow_p = K + ((size_t)kv * T + key) * kD + 8 * g;
+    const half_t* vcol = Vt + (size_t)kv * kD * T + key;
+  #pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      kf[kk] = live ? ld8(krow_p + 16 * kk) : half8{};
+  #pragma unroll
+      for (int e = 0; e < 8; ++e) vf[kk][e] = live ? vcol[(size_t)(16 * kk + 8 * g + e) * T] : (half_t)0;
+    }
+  }
+
+  half_t* const qb = reinterpret_cast<half_t*>(region[wave]);
+  half_t* const ob = qb + kTileHalfs;
+  float* const lt = reinterpret_cast<float*>(ob + kTileHalfs);  // [L][64], then [-D][64]
+  const float* const dt = lt + kTile;
+  const int sr = lane >> 3, sc = lane & 7;
+  const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<half_t*>(Q + (size_t)h * T * kD), 0, T * kD * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<half_t*>(dO + (size_t)h * kD), 0, (T * Hq - h) * kD * 2, kBufferWord3);
+  int4v st[16];  // the next tile: Q chunks 0..7, dO chunks 8..15
+  float rl = 0.0f, rd = 0.0f;
+  auto load = [&](int it) {
+    const int q0 = it * kTile;
+  #pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = q0 + sr + 8 * i;
+      st[i] = __builtin_amdgcn_raw_buffer_load_b128(qrsrc, (r * kD + sc * 8) * 2, 0, 0);
+      st[8 + i] = __builtin_amdgcn_raw_buffer_load_b128(
+          orsrc, (int)(((unsigned)r * (unsigned)Hq * kD + sc * 8) * 2u), 0, 0);
+    }
+    const int q = q0 + lane;  // queries past T: L = +inf and -D = 0, so P = 0
+    rl = q < T ? L[(size_t)h * T + q] : INFINITY;
+    rd = q < T ? -D[(size_t)h * T + q] : 0.0f;
+  };
+  auto store = [&]() {
+  #pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int off = chunk_offset(sr + 8 * i, sc);
+      *reinterpret_cast<int4v*>(qb + off) = st[i];
+      *reinterpret_cast<int4v*>(ob + off) = st[8 + i];
+    }
+    lt[lane] = rl;
+    lt[kTile + lane] = rd;
+  };
+
+  int nOff[4];
+  #pragma unroll
+  for (int kk = 0; kk < 4; ++kk) nOff[kk] = chunk_offset(krow(n), 2 * kk + g);
+  int tOff[2][2];
+  #pragma unroll
+  for (int mh = 0; mh < 2; ++mh)
+  #pragma unroll
+    for (int hi = 0; hi < 2; ++hi) tOff[mh][hi] = tr_offset(lane, false, mh, hi);
+
+  float16v dk0 = {}, dk1 = {}, dv0 = {}, dv1 = {};
+  int it = ft + wave;
+  if (PREFETCH && it < nt) load(it);
+  while (it < nt) {
+    if (!PREFETCH) load(it);
+    store();
+    __builtin_amdgcn_s_waitcnt(kLdsDone);
+    const int in = it + kSW;
+    if (PREFETCH && in < nt) load(in);
+    float16v nd0, nd1;
+  #pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float4v d0 = *reinterpret_cast<const float4v*>(dt + 16 * b + 8 * g);
+      const float4v d1 = *reinterpret_cast<const float4v*>(dt + 16 * b + 8 * g + 4);
+  #pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float16v& nd = b < 2 ? nd0 : nd1;
+        nd[8 * (b & 1) + e] = d0[e];
+        nd[8 * (b & 1) + 4 + e] = d1[e];
+      }
+    }
+    float16v s0, s1, p0, p1;
+  #pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      s0 = mfma(ld8(qb + nOff[kk]), kf[kk], kk == 0 ? float16v{} : s0);
+      s1 = mfma(ld8(qb + nOff[kk] + 32 * kRowHalfs), kf[kk], kk == 0 ? float16v{} : s1);
+      p0 = mfma(ld8(ob + nOff[kk]), vf[kk], kk == 0 ? nd0 : p0);
+      p1 = mfma(ld8(ob + nOff[kk] + 32 * kRowHalfs), vf[kk], kk == 0 ? nd1 : p1);
+    }
+    if (it * kTile < key0 + 31) {
+      const int lim = key - it * kTile - 8 * g;
+  #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int q = 16 * (i >> 3) + (i & 7);
+        if (q < lim) s0[i] = -INFINITY;
+        if (q + 32 < lim) s1[i] = -INFINITY;
+      }
+    }
+    half8 pb[4], db[4];
+  #pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int q = 16 * b + 8 * g;
+      const float4v l0 = *reinterpret_cast<const float4v*>(lt + q);
+      const float4v l1 = *reinterpret_cast<const float4v*>(lt + q + 4);
+  #pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 8 * (b & 1) + e;
+        const float sv = b < 2 ? s0[i] : s1[i];
+        const float pv = b < 2 ? p0[i] : p1[i];
+        const float lv = e < 4 ? l0[e] : l1[e - 4];
+        const float P = __builtin_amdgcn_exp2f(fmaf(sv, c, -lv));
+        pb[b][e] = (half_t)P;
+        db[b][e] = (half_t)(P * pv);
+      }
+    }
+  #pragma unroll
+    for (int ck = 0; ck < 4; ++ck) {
+      const half_t* oc = ob + 16 * ck * kRowHalfs;
+      const half_t* qc = qb + 16 * ck * kRowHalfs;
+      dv0 = mfma(tr8(oc, tOff[0][0], tOff[0][1]), pb[ck], dv0);
+      dv1 = mfma(tr8(oc, tOff[1][0], tOff[1][1]), pb[ck], dv1);
+      dk0 = mfma(tr8(qc, tOff[0][0], tOff[0][1]), db[ck], dk0);
+      dk1 = mfma(tr8(qc, tOff[1][0], tOff[1][1]), db[ck], dk1);
+    }
+    it = in;
+  }
+
+  // sum the four partials in wave order
+  float* const part = reinterpret_cast<float*>(region[wave]);  // [4][16][64]
+  if (wave > 0) {
+  #pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      part[i * 64 + lane] = dk0[i];
+      part[(16 + i) * 64 + lane] = dk1[i];
+      part[(32 + i) * 64 + lane] = dv0[i];
+      part[(48 + i) * 64 + lane] = dv1[i];
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  #pragma unroll
+  for (int w = 1; w < kSW; ++w) {
+    const float* pw = reinterpret_cast<const float*>(region[w]);
+  #pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dk0[i] += pw[i * 64 + lane];
+      dk1[i] += pw[(16 + i) * 64 + lane];
+      dv0[i] += pw[(32 + i) * 64 + lane];
+      dv1[i] += pw[(48 + i) * 64 + lane];
+    }
+  }
+  // accumulator element 4q + e of lane (n, g) is d = 8q + 4g + e of key n
+  if (live) {
+    float* kout = dKp + ((size_t)h * T + key) * kD + 4 * g;
+  #pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4v a = {dk0[4 * q], dk0[4 * q + 1], dk0[4 * q + 2], dk0[4 * q + 3]};
+      const float4v b = {dk1[4 * q], dk1[4 * q + 1], dk1[4 * q + 2], dk1[4 * q + 3]};
+      *reinterpret_cast<float4v*>(kout + 8 * q) = a * s;
+      *reinterpret_cast<float4v*>(kout + 32 + 8 * q) = b * s;
+    }
+    float* vout = dVp + (size_t)h * kD * T + key;
+  #pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int d = 8 * (i >> 2) + 4 * g + (i & 3);
+      vout[(size_t)d * T] = dv0[i];
+      vout[(size_t)(d + 32) * T] = dv1[i];
+    }
+  }
+}
+
+// -------------------------------------------------------------------------
 // Grouped gradient reduction: out[kv][e] = sum over z = 0..G-1, in order, of
 // planes[kv G + z][e], for the dK planes (blockIdx.z = 0) and the dV^T
 // planes (blockIdx.z = 1); a thread owns four consecutive elements.
@@ -572,18 +953,27 @@ int check_device() {
 // once for 256 rows and run a heavy block, then its light partner (blocks b
 // and n-1-b), so every workgroup carries the same causal work; they are used
 // when that grid still gives each of the 256 compute units a workgroup.
-// Otherwise four-wave workgroups (two per compute unit) run, paired the same
-// way when their halved grid still fills the compute units, and else one
-// block each, heaviest first: idle units cost more than the imbalance.
+// Below that, when even the four-wave grid of 128-row blocks would hold fewer
+// than two workgroups per compute unit, the split launches run (32-row
+// blocks, their tiles dealt over four waves), so a block's walk is four times
+// shorter.  Otherwise four-wave workgroups (two per compute unit) run, paired
+// the same way when their halved grid still fills the compute units, and
+// else one block each, heaviest first: idle units cost more than the
+// imbalance.
+constexpr long long kSplitBelow = 512;  // four-wave workgroups (128-row blocks x heads)
 struct Shape {
   int nw, nBlocks, nPairs;
-  bool paired;
+  bool paired, split;
 };
 Shape launch_shape(int T, int Hq) {
   const int n8 = (T + 255) / 256, n4 = (T + 127) / 128;
-  if (n8 > 1 && (long long)((n8 + 1) / 2) * Hq >= 256) return {8, n8, (n8 + 1) / 2, true};
+  if (n8 > 1 && (long long)((n8 + 1) / 2) * Hq >= 256) return {8, n8, (n8 + 1) / 2, true, false};
+  if ((long long)n4 * Hq < kSplitBelow) {
+    const int n = (T + 31) / 32;
+    return {kSW, n, n, false, true};
+  }
   const bool paired = n4 > 1 && (long long)((n4 + 1) / 2) * Hq >= 256;
-  return {4, n4, paired ? (n4 + 1) / 2 : n4, paired};
+  return {4, n4, paired ? (n4 + 1) / 2 : n4, paired, false};
 }
 
 void launch_query(const half_t* Q, const half_t* K, const half_t* Vt, const half_t* O,
@@ -593,6 +983,12 @@ void launch_query(const half_t* Q, const half_t* K, const half_t* Vt, const half
   const dim3 grid((unsigned)sh.nPairs * (unsigned)Hq);
   const int G = Hq / Hkv;
   const bool vec = T % 8 == 0;
+  if (sh.split) {
+    auto sk = vec ? sattn_bwdq_split_kernel<true, true> : sattn_bwdq_split_kernel<false, false>;
+    hipLaunchKernelGGL(sk, grid, dim3(64 * kSW), 0, stream, Q, K, Vt, O, dO, L, dQ, D, c, s, T, Hq,
+                       G, sh.nBlocks);
+    return;
+  }
   auto kernel = vec ? sattn_bwdq_kernel<8, true, true> : sattn_bwdq_kernel<8, false, true>;
   if (sh.nw == 4 && sh.paired)
     kernel = vec ? sattn_bwdq_kernel<4, true, true> : sattn_bwdq_kernel<4, false, true>;
@@ -610,10 +1006,15 @@ void launch_key(const half_t* Q, const half_t* K, const half_t* Vt, const half_t
   float* vp = G == 1 ? dVt : static_cast<float*>(ws) + (size_t)Hq * T * kD;
   const Shape sh = launch_shape(T, Hq);
   const dim3 grid((unsigned)sh.nPairs * (unsigned)Hq);
-  auto kernel = sattn_bwdk_kernel<8, true, true>;
-  if (sh.nw == 4) kernel = sh.paired ? sattn_bwdk_kernel<4, true, true> : sattn_bwdk_kernel<4, true, false>;
-  hipLaunchKernelGGL(kernel, grid, dim3(64 * sh.nw), 0, stream, Q, K, Vt, dO, L, D, kp, vp, c, s, T,
-                     Hq, G, sh.nBlocks, sh.nPairs);
+  if (sh.split) {
+    hipLaunchKernelGGL(sattn_bwdk_split_kernel<false>, grid, dim3(64 * kSW), 0, stream, Q, K, Vt, dO, L, D,
+                       kp, vp, c, s, T, Hq, G, sh.nBlocks);
+  } else {
+    auto kernel = sattn_bwdk_kernel<8, true, true>;
+    if (sh.nw == 4) kernel = sh.paired ? sattn_bwdk_kernel<4, true, true> : sattn_bwdk_kernel<4, true, false>;
+    hipLaunchKernelGGL(kernel, grid, dim3(64 * sh.nw), 0, stream, Q, K, Vt, dO, L, D, kp, vp, c, s, T,
+                       Hq, G, sh.nBlocks, sh.nPairs);
+  }
   if (G > 1) {
     const int planeQuads = T * kD / 4;
     const dim3 rgrid((unsigned)((planeQuads + 255) / 256), (unsigned)Hkv, 2u);

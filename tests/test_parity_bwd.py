@@ -16,7 +16,8 @@ pytestmark = pytest.mark.gpu
 
 # (T, Hq, Hkv, seed, generator options): tiny and degenerate shapes, ragged
 # tails, T not a multiple of 8 (scalar V^T staging), odd groups, the small
-# and medium forward workloads' shapes and value distributions
+# and medium forward workloads' shapes and value distributions (these take
+# the split launches: 32-row blocks, tiles dealt over four waves)
 FULL = [
     (1, 1, 1, 51, {}),
     (2, 2, 1, 52, {}),
@@ -36,6 +37,8 @@ FULL = [
     (512, 128, 16, 63, {}),
     (520, 128, 64, 62, {}),
     (777, 128, 64, 64, {}),
+    # one 128-row block over many heads: four-wave workgroups, unpaired
+    (100, 512, 8, 65, {}),
 ]
 
 
