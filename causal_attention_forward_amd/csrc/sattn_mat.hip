@@ -20,7 +20,12 @@
 //    v_mfma_f32_32x32x16_f16 chain over the 64 head-width columns with its
 //    operands straight from global memory (16-byte rows of Q and K).  In the
 //    accumulator a lane holds one key column, so the 32 lanes of a row store
-//    128 consecutive bytes.
+//    128 consecutive bytes.  The stores bypass the caches' allocation
+//    (non-temporal): the plane is written once and read back only by the
+//    next launch, and write-allocating it in L2 halved the write rate.  Each
+//    XCD takes a contiguous run of tiles (row by row), so a row's pieces
+//    leave one L2.
+//  * The softmax streams S in and P out the same way (non-temporal).
 //  * Softmax: one wave per row, 4-float reads per lane; the row (up to 4096
 //    keys) stays in registers while a running maximum and sum per lane are
 //    merged across the wave, then P is written from the registers, so S is
@@ -55,6 +60,16 @@ __device__ __forceinline__ float16v mfma(half8 a, half8 b, float16v c) {
 
 __device__ __forceinline__ half8 ld8(const half_t* p) { return *reinterpret_cast<const half8*>(p); }
 
+// Workgroups are dealt to the eight XCDs round-robin by linear index.  This
+// returns the workgroup's place (x fastest, then y) in an order where each
+// XCD receives one contiguous run, so consecutive tiles of a plane's rows
+// meet in one L2 before they go to HBM.
+__device__ __forceinline__ int xcd_linear() {
+  const int n = gridDim.x * gridDim.y, b = blockIdx.y * gridDim.x + blockIdx.x;
+  const int xcd = b % 8, idx = b / 8;
+  return xcd * (n / 8) + min(xcd, n % 8) + idx;
+}
+
 // -------------------------------------------------------------------------
 // 1. scores.  Grid (nt (nt+1) / 2 lower-triangle 64 x 64 tiles, Hq), 256
 // threads: wave w computes the 32 x 32 block (w / 2, w % 2) of its tile.
@@ -62,7 +77,8 @@ __device__ __forceinline__ half8 ld8(const half_t* p) { return *reinterpret_cast
 __global__ void __launch_bounds__(256)
 sattn_mat_scores_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
                         float* __restrict__ S, float c, int T, int G) {
-  const int tile = blockIdx.x, h = blockIdx.y, kv = h / G;
+  const int lin = xcd_linear();
+  const int tile = lin % gridDim.x, h = lin / gridDim.x, kv = h / G;
   // tile = it (it + 1) / 2 + jt with 0 <= jt <= it
   int it = (int)((sqrtf(8.0f * (float)tile + 1.0f) - 1.0f) * 0.5f);
   while ((it + 1) * (it + 2) / 2 <= tile) ++it;
@@ -86,7 +102,7 @@ sattn_mat_scores_kernel(const half_t* __restrict__ Q, const half_t* __restrict__
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = i0 + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (i < T && jb <= i) col[(size_t)i * T] = acc[r] * c;
+      if (i < T && jb <= i) __builtin_nontemporal_store(acc[r] * c, col + (size_t)i * T);
     }
   }
 }
@@ -118,7 +134,9 @@ sattn_mat_softmax_kernel(const float* __restrict__ S, half_t* __restrict__ P,
   auto chunk = [&](int base, float (&v)[4]) {
     const int j = base + 4 * lane;
     if (VEC && j + 3 < cnt) {
-      const float4v x = *reinterpret_cast<const float4v*>(s + j);
+      // read once when the row stays in registers (NCH > 0): stream it past L2
+      const float4v x = NCH > 0 ? __builtin_nontemporal_load(reinterpret_cast<const float4v*>(s + j))
+                                : *reinterpret_cast<const float4v*>(s + j);
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = x[e];
     } else {
@@ -143,7 +161,7 @@ sattn_mat_softmax_kernel(const float* __restrict__ S, half_t* __restrict__ P,
       half4 y;
 #pragma unroll
       for (int e = 0; e < 4; ++e) y[e] = (half_t)__builtin_amdgcn_exp2f(v[e] - lse);
-      *reinterpret_cast<half4*>(p + j) = y;
+      __builtin_nontemporal_store(y, reinterpret_cast<half4*>(p + j));
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
