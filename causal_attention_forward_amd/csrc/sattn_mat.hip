@@ -31,10 +31,11 @@
 //    merged across the wave, then P is written from the registers, so S is
 //    read once; longer rows are read twice.  HBM-bound.
 //  * P V: a workgroup takes 128 query rows of a head (a wave 32 rows x all
-//    64 columns) and stages each 64-key V^T tile in LDS once for its four
-//    waves; P rows are 16-byte reads straight from global memory.  Keys past
-//    the row (only in the diagonal tile) are masked in registers, so the
-//    planes' memory above the diagonal is never read into a result.
+//    64 columns) and stages each 64-key V^T tile and the 128 x 64 tile of P
+//    rows in LDS once for its four waves (coalesced loads; P swizzled so the
+//    operand reads hit every bank once).  Keys past the row (only in the
+//    diagonal tile) are masked in registers, so the planes' memory above the
+//    diagonal is never read into a result.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -43,6 +44,7 @@
 #include <atomic>
 
 #include "sattn.h"
+#include "sattn_lds.h"
 
 namespace {
 
@@ -207,18 +209,22 @@ sattn_mat_softmax_kernel(const float* __restrict__ S, half_t* __restrict__ P,
 // -------------------------------------------------------------------------
 // 3. P V.  Grid (ceil(T / 128) row blocks, heaviest first; Hq), 256 threads:
 // wave w takes query rows 128 rb + 32 w .. +31 and all 64 head-width
-// columns; the workgroup stages each 64-key V^T tile in LDS once for its four
-// waves (double-buffered), and each wave reads its P rows straight from
-// global memory, four 16-byte reads per tile issued before the products.
+// columns.  Per 64-key tile the workgroup stages the V^T tile and the
+// 128 x 64 tile of P rows in LDS once (coalesced 16-byte loads, double-
+// buffered); the waves take their P operands from the swizzled P tile.  Keys
+// past a row (only in the diagonal tile) are masked in registers, so the
+// plane's memory above the diagonal is never read into a result.
 // -------------------------------------------------------------------------
 constexpr int kRowHalfs = kD + 8;  // V^T tile row in LDS: 64 keys + 16 bytes of padding
 constexpr int kTileHalfs = kD * kRowHalfs;
+constexpr int kPTileHalfs = 128 * sattn_lds::kRowHalfs;  // P tile: 128 rows x 64 keys, swizzled
 
 template <bool VEC>
 __global__ void __launch_bounds__(256)
 sattn_mat_pv_kernel(const half_t* __restrict__ P, const half_t* __restrict__ Vt,
                     half_t* __restrict__ O, int T, int Hq, int G, int nRowBlocks) {
   __shared__ __attribute__((aligned(16))) half_t vbuf[2 * kTileHalfs];
+  __shared__ __attribute__((aligned(16))) half_t pbuf[2 * kPTileHalfs];
   const int h = blockIdx.y, kv = h / G;
   const int rb = nRowBlocks - 1 - (int)blockIdx.x;
   const int tid = threadIdx.x;
@@ -227,16 +233,19 @@ sattn_mat_pv_kernel(const half_t* __restrict__ P, const half_t* __restrict__ Vt,
   const int i0 = row0 + 32 * wave;
   const int ia = i0 + n;
   const int nkt = (min(T, row0 + 128) - 1) / 64 + 1;  // key tiles of the workgroup
-  const half_t* prow = P + ((size_t)h * T + min(ia, T - 1)) * T;
   const half_t* Vh = Vt + (size_t)kv * kD * T;
-  // staging: thread t owns 16-byte chunks t and t + 256 of a V^T tile
-  // (row d = c / 8, keys 8 (c % 8) ..)
+  const half_t* Ph = P + (size_t)h * T * T;
+  // staging: thread t owns 16-byte chunks t and t + 256 of the V^T tile (row
+  // d = c / 8, keys 8 (c % 8) ..) and chunks t + 256 k (k < 4) of the P tile
+  // (row c / 8 of the block, keys 8 (c % 8) ..); rows past T, and keys past T
+  // of a row, read as zeros
   const int cr = tid >> 3, cc = tid & 7;
-  half8 st[2];
+  half8 st[2], sp[4];
   auto load = [&](int kt) {
+    const int key = kt * 64 + cc * 8;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const int d = cr + 32 * p, key = kt * 64 + cc * 8;
+      const int d = cr + 32 * p;
       if (VEC && key + 7 < T) {
         st[p] = ld8(Vh + (size_t)d * T + key);
       } else {
@@ -244,11 +253,25 @@ sattn_mat_pv_kernel(const half_t* __restrict__ P, const half_t* __restrict__ Vt,
         for (int e = 0; e < 8; ++e) st[p][e] = key + e < T ? Vh[(size_t)d * T + key + e] : (half_t)0;
       }
     }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = row0 + cr + 32 * p;
+      const half_t* src = Ph + (size_t)min(r, T - 1) * T + key;
+      if (VEC && r < T && key + 7 < T) {
+        sp[p] = ld8(src);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sp[p][e] = (r < T && key + e < T) ? src[e] : (half_t)0;
+      }
+    }
   };
   auto store = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < 2; ++p)
       *reinterpret_cast<half8*>(vbuf + buf * kTileHalfs + (cr + 32 * p) * kRowHalfs + cc * 8) = st[p];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      *reinterpret_cast<half8*>(pbuf + buf * kPTileHalfs + sattn_lds::chunk_offset(cr + 32 * p, cc)) = sp[p];
   };
   float16v acc0 = {}, acc1 = {};
   load(0);
@@ -259,14 +282,15 @@ sattn_mat_pv_kernel(const half_t* __restrict__ P, const half_t* __restrict__ Vt,
     if (kt + 1 < nkt) load(kt + 1);
     if (kt * 64 <= i0 + 31 && i0 < T) {
       half8 a[4];
+      const half_t* pb = pbuf + buf * kPTileHalfs;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int ja = kt * 64 + 16 * u + 8 * g;  // this lane's eight keys
-        if (VEC && ia < T && ja + 7 <= ia) {
-          a[u] = ld8(prow + ja);
-        } else {
+        a[u] = ld8(pb + sattn_lds::chunk_offset(32 * wave + n, 2 * u + g));
+        if (kt * 64 + 63 > i0) {  // the diagonal tile: keys past the row are zero
+          const int ja = kt * 64 + 16 * u + 8 * g;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) a[u][e] = (ia < T && ja + e <= ia) ? prow[ja + e] : (half_t)0;
+          for (int e = 0; e < 8; ++e)
+            if (ja + e > ia) a[u][e] = (half_t)0;
         }
       }
       const half_t* vb = vbuf + buf * kTileHalfs + n * kRowHalfs + 8 * g;
