@@ -114,8 +114,8 @@ int sattn_fwd_check(const void* Q, const void* K, const void* Vt, const void* O,
  * operands of the products that follow; every sum is binary32.  With
  * c = s log2(e) and the forward's own O and L these are the gradients of
  * sum(dO * O) with respect to Q, K and V.  Deterministic: no atomics, and
- * the group sum is taken in a fixed order, so the same inputs give the same
- * bits on every run.
+ * every sum, the group sum included, is taken in an order fixed by T and Hq,
+ * so the same inputs give the same bits on every run.
  *
  * Shared arguments (layouts as in sattn_fwd):
  *   Q    device, binary16 [Hq][T][64];  K  device, binary16 [Hkv][T][64]
