@@ -300,23 +300,46 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
     }
   };
 
-#pragma nounroll
-  for (int task = 0; task < 2; ++task) {
+  auto tiles_of = [&](int task) -> int {
     int nkt = 0;
 #pragma unroll
     for (int s = 0; s < RS; ++s) nkt = max(nkt, need_of(block_of(task, s)));
+    return nkt;
+  };
+  // A task's Q rows and first K and V^T tiles, loaded into registers before
+  // the task starts: for the second task, ahead of the first task's O
+  // stores, whose completion the wait for these loads would otherwise
+  // include (the vector memory counter retires loads and stores in order).
+  half8 qn[4];
+  Stage pk[2], setK[2], setV[2];
+  auto prefetch = [&](int task) {
+    const int blk = block_of(task, slot);
+    const int need = need_of(blk);
+    const int row = 32 * max(blk, 0) + n;
+    const half_t* qrow = Q + ((size_t)h * T + row) * kD + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qn[kk] = (need > 0 && row < T) ? *reinterpret_cast<const half8*>(qrow + 16 * kk) : half8{};
+    load_k(0, pk[0]);
+    load_k(1, pk[1]);
+    load_k(2, setK[0]);
+    load_v(0, setV[0]);
+    load_k(3, setK[1]);
+    load_v(1, setV[1]);
+  };
+  prefetch(0);
+
+#pragma nounroll
+  for (int task = 0; task < 2; ++task) {
+    const int nkt = tiles_of(task);
     if (nkt == 0) break;
     const int blk = block_of(task, slot);
     const int need = need_of(blk);
     const int row = 32 * max(blk, 0) + n;
 
     half8 qf[4];
-    {
-      const half_t* qrow = Q + ((size_t)h * T + row) * kD + 8 * g;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        qf[kk] = (need > 0 && row < T) ? *reinterpret_cast<const half8*>(qrow + 16 * kk) : half8{};
-    }
+    for (int kk = 0; kk < 4; ++kk) qf[kk] = qn[kk];
     float m = -INFINITY, l = 0.0f;
     float16v o0 = {}, o1 = {};
     float16v sa0, sa1, sb0, sb1;
@@ -480,19 +503,8 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
 
     // Ring schedule: K tile t is read at steps t-1 (S of t) and t (overflow
     // fallback), V^T tile t at step t+1 (P V of t); see the stage itself.
-    Stage setK[2], setV[2];
-    {
-      // every load of the prologue in flight before the first store waits
-      Stage k0, k1;
-      load_k(0, k0);
-      load_k(1, k1);
-      load_k(2, setK[0]);
-      load_v(0, setV[0]);
-      load_k(3, setK[1]);
-      load_v(1, setV[1]);
-      store_k(0, k0);
-      store_k(1, k1);
-    }
+    store_k(0, pk[0]);
+    store_k(1, pk[1]);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     barrier();
     // Loads past the last tile read zeros and stores of them land in ring
@@ -568,12 +580,18 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
 #pragma unroll
       for (int i = 0; i < 4; ++i) pa[i] = pb[i];
     }
+    float inv = 0.0f, lse = 0.0f;
     if (need > 0) {
       stage_any(j);
       pv((j + kVRing - 1) % kVRing, pa);
       const float lt = l + xlane(l, swapAddr);
-      const float inv = __builtin_amdgcn_rcpf(lt);
-      const float lse = m + __builtin_amdgcn_logf(lt);
+      inv = __builtin_amdgcn_rcpf(lt);
+      lse = m + __builtin_amdgcn_logf(lt);
+      ++j;
+    }
+    for (; j <= nkt; ++j) stage_any(j);
+    if (task == 0 && tiles_of(1) > 0) prefetch(1);
+    if (need > 0) {
       if (row < T) {
         half_t* orow = O + (size_t)row * Hq * kD + (size_t)h * kD + 4 * g;
 #pragma unroll
@@ -585,9 +603,7 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
         }
         if (g == 0) L[(size_t)h * T + row] = lse;
       }
-      ++j;
     }
-    for (; j <= nkt; ++j) stage_any(j);
     barrier();
   }
 }
