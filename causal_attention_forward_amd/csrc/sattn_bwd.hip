@@ -128,8 +128,8 @@ sattn_bwdq_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
                   float* __restrict__ dQ, float* __restrict__ D, float c, float s, int T, int Hq,
                   int G, int nBlocks, int nPairs) {
   __shared__ __attribute__((aligned(16))) half_t smem[4 * kTileHalfs];
-  half_t* const kbuf = smem;                   // K tiles [2][64 keys][72]
-  half_t* const vbuf = smem + 2 * kTileHalfs;  // V^T tiles [2][64 d][72]
+  half_t* const kbuf = smem;                   // K tiles [2][64 keys][64], chunks swizzled
+  half_t* const vbuf = smem + 2 * kTileHalfs;  // V^T tiles [2][64 d][64], chunks swizzled
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -324,8 +324,8 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
                   int Hq, int G, int nBlocks, int nPairs) {
   __shared__ __attribute__((aligned(16))) half_t smem[4 * kTileHalfs];
   __shared__ __attribute__((aligned(16))) float rowterms[2][2][kTile];  // [buf][L, D][query]
-  half_t* const qbuf = smem;                    // Q tiles [2][64 queries][72]
-  half_t* const obuf = smem + 2 * kTileHalfs;   // dO tiles [2][64 queries][72]
+  half_t* const qbuf = smem;                    // Q tiles [2][64 queries][64], chunks swizzled
+  half_t* const obuf = smem + 2 * kTileHalfs;   // dO tiles [2][64 queries][64], chunks swizzled
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

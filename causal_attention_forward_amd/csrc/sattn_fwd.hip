@@ -174,6 +174,8 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
   constexpr float kSumCap = 256.0f;        // 2^kLazy
   constexpr int kOutOfRange = 0x7FFFFFF0;  // a buffer offset past every range
   __shared__ __attribute__((aligned(16))) half_t smem[(kKRing + kVRing) * kTileHalfs];
+  // each wave's 32 O rows on their way to global memory (see the epilogue)
+  __shared__ __attribute__((aligned(16))) half_t obuf[kNW][32 * kRowHalfs];
   half_t* const kring = smem;
   half_t* const vring = smem + kKRing * kTileHalfs;
   constexpr int kTileBytes = kTileHalfs * 2;
@@ -592,17 +594,29 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
     for (; j <= nkt; ++j) stage_any(j);
     if (task == 0 && tiles_of(1) > 0) prefetch(1);
     if (need > 0) {
-      if (row < T) {
-        half_t* orow = O + (size_t)row * Hq * kD + (size_t)h * kD + 4 * g;
+      // O goes through the wave's own LDS rows so that each global store
+      // writes whole 128-byte row segments (eight lanes a row) rather than
+      // 8 bytes in each of 32 rows.  Accumulator element 4 q4 + e of lane
+      // (n, g) is d = 8 q4 + 4 g + e (o1: d + 32) of row n.  The wave reads
+      // back only what it wrote, and a wave's LDS accesses complete in order.
+      half_t* const ob = obuf[wave];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4v va = {o0[4 * q4], o0[4 * q4 + 1], o0[4 * q4 + 2], o0[4 * q4 + 3]};
-          const float4v vb = {o1[4 * q4], o1[4 * q4 + 1], o1[4 * q4 + 2], o1[4 * q4 + 3]};
-          *reinterpret_cast<half4*>(orow + 8 * q4) = __builtin_convertvector(va * inv, half4);
-          *reinterpret_cast<half4*>(orow + 32 + 8 * q4) = __builtin_convertvector(vb * inv, half4);
-        }
-        if (g == 0) L[(size_t)h * T + row] = lse;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4v va = {o0[4 * q4], o0[4 * q4 + 1], o0[4 * q4 + 2], o0[4 * q4 + 3]};
+        const float4v vb = {o1[4 * q4], o1[4 * q4 + 1], o1[4 * q4 + 2], o1[4 * q4 + 3]};
+        half_t* const orow = ob + n * kRowHalfs + 8 * q4 + 4 * g;
+        *reinterpret_cast<half4*>(orow) = __builtin_convertvector(va * inv, half4);
+        *reinterpret_cast<half4*>(orow + 32) = __builtin_convertvector(vb * inv, half4);
       }
+      const int row0 = 32 * blk, rr = lane >> 3, ch = lane & 7;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {  // rows 8p + lane/8, 16-byte chunk lane%8
+        const int r = 8 * p + rr;
+        const int4v v = *reinterpret_cast<const int4v*>(ob + r * kRowHalfs + 8 * ch);
+        if (row0 + r < T)
+          *reinterpret_cast<int4v*>(O + (size_t)(row0 + r) * Hq * kD + (size_t)h * kD + 8 * ch) = v;
+      }
+      if (row < T && g == 0) L[(size_t)h * T + row] = lse;
     }
     barrier();
   }
