@@ -234,47 +234,55 @@ sattn_fwd_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ 
   // merge the four waves' (m, l, O) of the same 32 rows; l is a partial sum
   // per lane (keys of its half), so the pair's sums are added first
   l += xlane(l, swapAddr);
-  float* const part = reinterpret_cast<float*>(region[wave]);  // [2][16][64] O^T, [64] m, [64] l
-  if (wave > 0) {
+  // Each wave leaves its O rows (binary32, row-major, 68-float rows), its m
+  // and its l in its own region; then wave w merges rows 8w .. 8w+7 of all
+  // four in wave order and writes them as whole 128-byte rows (eight lanes a
+  // row).  Accumulator element 4 q + e of lane (n, g) is d = 8 q + 4 g + e
+  // (o1: d + 32) of row n.
+  constexpr int kPartRow = kD + 4;
+  float* const part = reinterpret_cast<float*>(region[wave]);  // [32][68] O, [64] m, [64] l
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      part[i * 64 + lane] = o0[i];
-      part[(16 + i) * 64 + lane] = o1[i];
-    }
-    part[32 * 64 + lane] = m;
-    part[33 * 64 + lane] = l;
+  for (int q = 0; q < 4; ++q) {
+    const float4v va = {o0[4 * q], o0[4 * q + 1], o0[4 * q + 2], o0[4 * q + 3]};
+    const float4v vb = {o1[4 * q], o1[4 * q + 1], o1[4 * q + 2], o1[4 * q + 3]};
+    *reinterpret_cast<float4v*>(part + n * kPartRow + 8 * q + 4 * g) = va;
+    *reinterpret_cast<float4v*>(part + n * kPartRow + 32 + 8 * q + 4 * g) = vb;
   }
+  part[32 * kPartRow + lane] = m;
+  part[32 * kPartRow + 64 + lane] = l;
   __syncthreads();
-  if (wave != 0) return;
-  float M = m;
+  const int r = 8 * wave + (lane >> 3), ch = lane & 7;  // row r, columns 8 ch .. 8 ch + 7
+  const float* p0 = reinterpret_cast<const float*>(region[0]);
+  float M = p0[32 * kPartRow + r];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, reinterpret_cast<const float*>(region[w])[32 * 64 + lane]);
-  const float a0 = __builtin_amdgcn_exp2f(m - M);
-  float lt = l * a0;
-  o0 *= a0;
-  o1 *= a0;
+  for (int w = 1; w < kWaves; ++w)
+    M = fmaxf(M, reinterpret_cast<const float*>(region[w])[32 * kPartRow + r]);
+  float lt = 0.0f;
+  float4v ya = {}, yb = {};
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) {
+  for (int w = 0; w < kWaves; ++w) {
     const float* pw = reinterpret_cast<const float*>(region[w]);
-    const float aw = __builtin_amdgcn_exp2f(pw[32 * 64 + lane] - M);  // 0 for a wave with no tile
-    lt += pw[33 * 64 + lane] * aw;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      o0[i] += pw[i * 64 + lane] * aw;
-      o1[i] += pw[(16 + i) * 64 + lane] * aw;
+    const float aw = __builtin_amdgcn_exp2f(pw[32 * kPartRow + r] - M);  // 0 for a wave with no tile
+    const float4v xa = *reinterpret_cast<const float4v*>(pw + r * kPartRow + 8 * ch);
+    const float4v xb = *reinterpret_cast<const float4v*>(pw + r * kPartRow + 8 * ch + 4);
+    if (w == 0) {
+      lt = pw[32 * kPartRow + 64 + r] * aw;
+      ya = xa * aw;
+      yb = xb * aw;
+    } else {
+      lt += pw[32 * kPartRow + 64 + r] * aw;
+      ya += xa * aw;
+      yb += xb * aw;
     }
   }
-  if (row < T) {
+  const int orow = 32 * blk + r;
+  if (orow < T) {
     const float inv = __builtin_amdgcn_rcpf(lt);
-    half_t* orow = O + (size_t)row * Hq * kD + (size_t)h * kD + 4 * g;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float4v va = {o0[4 * q4], o0[4 * q4 + 1], o0[4 * q4 + 2], o0[4 * q4 + 3]};
-      const float4v vb = {o1[4 * q4], o1[4 * q4 + 1], o1[4 * q4 + 2], o1[4 * q4 + 3]};
-      *reinterpret_cast<half4*>(orow + 8 * q4) = __builtin_convertvector(va * inv, half4);
-      *reinterpret_cast<half4*>(orow + 32 + 8 * q4) = __builtin_convertvector(vb * inv, half4);
-    }
-    if (g == 0) L[(size_t)h * T + row] = M + __builtin_amdgcn_logf(lt);
+    const half4 ha = __builtin_convertvector(ya * inv, half4);
+    const half4 hb = __builtin_convertvector(yb * inv, half4);
+    const half8 o8 = {ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
+    *reinterpret_cast<half8*>(O + (size_t)orow * Hq * kD + (size_t)h * kD + 8 * ch) = o8;
+    if (ch == 0) L[(size_t)h * T + orow] = M + __builtin_amdgcn_logf(lt);
   }
 }
 
