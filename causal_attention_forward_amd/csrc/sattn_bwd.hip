@@ -540,6 +540,45 @@ sattn_bwdk_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
 // result is deterministic.  The tile bodies are those of the launches above.
 // -------------------------------------------------------------------------
 constexpr int kSW = 4;  // waves per workgroup of the split launches
+constexpr int kPartRow = kD + 4;  // floats per row of a partial in LDS
+
+// A wave's 32 x 64 binary32 partial, row-major with kPartRow-float rows, from
+// its accumulators: element 4q + e of lane (n, g) is column 8q + 4g + e of row
+// n (a1: column + 32).
+__device__ __forceinline__ void store_partial_rows(float* part, const float16v& a0,
+                                                   const float16v& a1, int lane) {
+  const int n = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4v a = {a0[4 * q], a0[4 * q + 1], a0[4 * q + 2], a0[4 * q + 3]};
+    const float4v b = {a1[4 * q], a1[4 * q + 1], a1[4 * q + 2], a1[4 * q + 3]};
+    *reinterpret_cast<float4v*>(part + n * kPartRow + 8 * q + 4 * g) = a;
+    *reinterpret_cast<float4v*>(part + n * kPartRow + 32 + 8 * q + 4 * g) = b;
+  }
+}
+
+// Rows 8 wave .. 8 wave + 7 of the sum of the kSW partials (in wave order),
+// times s, to out rows row0 + r < T: lane l takes row 8 wave + l/8, columns
+// 8(l%8) .. +7.
+template <typename Region>
+__device__ __forceinline__ void sum_rows_out(const Region& region, float* out, int row0, int T,
+                                             float s, int wave, int lane) {
+  const int r = 8 * wave + (lane >> 3), ch = lane & 7;
+  const float* p0 = reinterpret_cast<const float*>(region[0]) + r * kPartRow + 8 * ch;
+  float4v a = *reinterpret_cast<const float4v*>(p0);
+  float4v b = *reinterpret_cast<const float4v*>(p0 + 4);
+#pragma unroll
+  for (int w = 1; w < kSW; ++w) {
+    const float* pw = reinterpret_cast<const float*>(region[w]) + r * kPartRow + 8 * ch;
+    a += *reinterpret_cast<const float4v*>(pw);
+    b += *reinterpret_cast<const float4v*>(pw + 4);
+  }
+  if (row0 + r < T) {
+    float* const o = out + (size_t)(row0 + r) * kD + 8 * ch;
+    *reinterpret_cast<float4v*>(o) = a * s;
+    *reinterpret_cast<float4v*>(o + 4) = b * s;
+  }
+}
 
 template <bool VT_VEC, bool PREFETCH>
 __global__ void __launch_bounds__(64 * kSW, 2)
@@ -684,36 +723,12 @@ sattn_bwdq_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__
     kt = kn;
   }
 
-  // sum the four partials in wave order
-  float* const part = reinterpret_cast<float*>(region[wave]);
-  if (wave > 0) {
-  #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      part[i * 64 + lane] = dq0[i];
-      part[(16 + i) * 64 + lane] = dq1[i];
-    }
-  }
+  // Sum the four partials in wave order: every wave leaves its partial in its
+  // region (row-major), then wave w sums rows 8w .. 8w+7 and writes them as
+  // whole 256-byte rows (eight lanes a row).
+  store_partial_rows(reinterpret_cast<float*>(region[wave]), dq0, dq1, lane);
   __syncthreads();
-  if (wave != 0) return;
-  #pragma unroll
-  for (int w = 1; w < kSW; ++w) {
-    const float* pw = reinterpret_cast<const float*>(region[w]);
-  #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dq0[i] += pw[i * 64 + lane];
-      dq1[i] += pw[(16 + i) * 64 + lane];
-    }
-  }
-  if (live) {
-    float* out = dQ + ((size_t)h * T + row) * kD + 4 * g;
-  #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4v a = {dq0[4 * q], dq0[4 * q + 1], dq0[4 * q + 2], dq0[4 * q + 3]};
-      const float4v b = {dq1[4 * q], dq1[4 * q + 1], dq1[4 * q + 2], dq1[4 * q + 3]};
-      *reinterpret_cast<float4v*>(out + 8 * q) = a * s;
-      *reinterpret_cast<float4v*>(out + 32 + 8 * q) = b * s;
-    }
-  }
+  sum_rows_out(region, dQ + (size_t)h * T * kD, 32 * blk, T, s, wave, lane);
 }
 
 template <bool PREFETCH>
@@ -868,47 +883,32 @@ sattn_bwdk_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__
     it = in;
   }
 
-  // sum the four partials in wave order
-  float* const part = reinterpret_cast<float*>(region[wave]);  // [4][16][64]
-  if (wave > 0) {
+  // Sum the four partials in wave order: every wave leaves its dK^T partial
+  // (row-major) and its dV^T partial (accumulator order) in its region; wave
+  // w then sums keys 8w .. 8w+7 of dK^T, written as whole 256-byte rows, and
+  // d rows 16w .. 16w+15 of dV^T, written 32 consecutive keys a row.
+  float* const part = reinterpret_cast<float*>(region[wave]);
+  store_partial_rows(part, dk0, dk1, lane);
+  float* const vpart = part + 32 * kPartRow;  // [32][64]: accumulator element i of dv0, dv1
   #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      part[i * 64 + lane] = dk0[i];
-      part[(16 + i) * 64 + lane] = dk1[i];
-      part[(32 + i) * 64 + lane] = dv0[i];
-      part[(48 + i) * 64 + lane] = dv1[i];
-    }
+  for (int i = 0; i < 16; ++i) {
+    vpart[i * 64 + lane] = dv0[i];
+    vpart[(16 + i) * 64 + lane] = dv1[i];
   }
   __syncthreads();
-  if (wave != 0) return;
+  sum_rows_out(region, dKp + (size_t)h * T * kD, key0, T, s, wave, lane);
+  // dV^T row d, key n: element 4(d%32/8) + d%4 of lane n + 32((d/4)%2), of dv1 if d >= 32
+  const int kn = lane & 31;
   #pragma unroll
-  for (int w = 1; w < kSW; ++w) {
-    const float* pw = reinterpret_cast<const float*>(region[w]);
+  for (int j = 0; j < 8; ++j) {
+    const int d = 16 * wave + 2 * j + (lane >> 5);
+    const int dd = d & 31;
+    const int idx = (d >= 32 ? 16 : 0) + 4 * (dd >> 3) + (dd & 3);
+    const int src = idx * 64 + kn + 32 * ((dd >> 2) & 1);
+    float v = reinterpret_cast<const float*>(region[0])[32 * kPartRow + src];
   #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dk0[i] += pw[i * 64 + lane];
-      dk1[i] += pw[(16 + i) * 64 + lane];
-      dv0[i] += pw[(32 + i) * 64 + lane];
-      dv1[i] += pw[(48 + i) * 64 + lane];
-    }
-  }
-  // accumulator element 4q + e of lane (n, g) is d = 8q + 4g + e of key n
-  if (live) {
-    float* kout = dKp + ((size_t)h * T + key) * kD + 4 * g;
-  #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4v a = {dk0[4 * q], dk0[4 * q + 1], dk0[4 * q + 2], dk0[4 * q + 3]};
-      const float4v b = {dk1[4 * q], dk1[4 * q + 1], dk1[4 * q + 2], dk1[4 * q + 3]};
-      *reinterpret_cast<float4v*>(kout + 8 * q) = a * s;
-      *reinterpret_cast<float4v*>(kout + 32 + 8 * q) = b * s;
-    }
-    float* vout = dVp + (size_t)h * kD * T + key;
-  #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int d = 8 * (i >> 2) + 4 * g + (i & 3);
-      vout[(size_t)d * T] = dv0[i];
-      vout[(size_t)(d + 32) * T] = dv1[i];
-    }
+    for (int w = 1; w < kSW; ++w) v += reinterpret_cast<const float*>(region[w])[32 * kPartRow + src];
+    if (key0 + kn < T) dVp[(size_t)h * kD * T + (size_t)d * T + key0 + kn] = v;
   }
 }
 
