@@ -49,6 +49,11 @@
 //    block's last tile (the one crossing its diagonal) is masked.  Rows past
 //    T are computed on zero queries and not stored, so T need not be a
 //    multiple of 64.
+//  * A block's end: each wave writes its O rows into its own LDS rows and
+//    reads them back row-major, so its global stores write whole 128-byte
+//    row segments; the light block's Q rows and first tiles are loaded before
+//    the heavy block's O stores, whose completion the vector memory counter
+//    would otherwise make those loads wait for.
 //  * Workgroups are dealt to the eight XCDs round-robin; they are renumbered
 //    so that each XCD receives a contiguous run ordered K/V head first,
 //    keeping one K/V head's tiles in one XCD's L2.

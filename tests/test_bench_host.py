@@ -47,3 +47,14 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_kernel_sha_ignores_comments_but_not_code(tmp_path):
+    a = tmp_path / "a.hip"
+    b = tmp_path / "b.hip"
+    c = tmp_path / "c.hip"
+    a.write_text("// header\nint f(int x) {  /* note */\n  return x + 1;  // one\n}\n")
+    b.write_text("int f(int x)\n{\n  return x + 1;\n}\n// trailing remark\n")
+    c.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.kernel_sha(str(a)) == bench.kernel_sha(str(b))
+    assert bench.kernel_sha(str(a)) != bench.kernel_sha(str(c))
