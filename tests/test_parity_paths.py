@@ -9,8 +9,8 @@ split-key kernel otherwise).
   more than 128 base-2 units, so 2^(t - m) overflows binary32 and the tile's
   scores are formed again and the reference taken from their maximum; the
   second spike falls inside the diagonal (masked) tile of some rows.
-* Shapes whose grid selects the eight-wave workgroup with T % 8 != 0, and
-  with two or one query heads per K/V head.
+* Shapes whose grid selects the eight-wave workgroup with T % 8 != 0, with
+  two or one query heads per K/V head, and with an odd number of query blocks.
 Full oracle comparison where it runs in seconds, sampled rows otherwise.
 """
 import numpy as np
@@ -89,8 +89,12 @@ def test_score_spikes(sattn, dev, shape):
         assert np.abs(O[k2:, h * 64:(h + 1) * 64] - v2[None, :]).max() <= TOL_O
 
 
-@pytest.mark.parametrize("shape", [(4095, 32, 8), (8192, 16, 8), (8192, 16, 16)])
+@pytest.mark.parametrize("shape", [(4095, 32, 8), (8192, 16, 8), (8192, 16, 16),
+                                   (4000, 32, 8), (3969, 32, 8)])
 def test_eight_wave_shapes(sattn, dev, shape):
+    """T=4000 and 3969 give 125 query blocks: the middle block has no light
+    partner and the last slot group's second slot is empty (3969 also takes
+    the scalar V^T staging)."""
     T, hq, hkv = shape
     note(f"eight-wave grid T={T} Hq={hq} Hkv={hkv}")
     x = make_inputs(T, hq, hkv, seed=23, peaked_fraction=0.01)
