@@ -560,10 +560,11 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
       l += exp_tile(sa0, sa1);
       round_p(sa0, sa1, pa);
     }
-    // Every wave runs stage(j) for j = 1 .. nkt in order (the workgroup's
-    // barriers); its own steps end at its own last tile: steady steps
-    // 1 .. need-2 (two per trip, S and P sets alternating), the masked step
-    // need-1, then P V of tile need-1 and the epilogue at step need.
+    // Every wave runs stage(j) for j = 1 .. nkt-1 in order (the workgroup's
+    // barriers; stage nkt would only stage tiles past every wave's last, so
+    // all waves skip it); its own steps end at its own last tile: steady
+    // steps 1 .. need-2 (two per trip, S and P sets alternating), the masked
+    // step need-1, then P V of tile need-1 and the epilogue at step need.
     int j = 1;
     for (; j + 2 < need; j += 2) {
       stage(P1{}, j);
@@ -589,14 +590,14 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
     }
     float inv = 0.0f, lse = 0.0f;
     if (need > 0) {
-      stage_any(j);
+      if (j < nkt) stage_any(j);
       pv((j + kVRing - 1) % kVRing, pa);
       const float lt = l + xlane(l, swapAddr);
       inv = __builtin_amdgcn_rcpf(lt);
       lse = m + __builtin_amdgcn_logf(lt);
       ++j;
     }
-    for (; j <= nkt; ++j) stage_any(j);
+    for (; j < nkt; ++j) stage_any(j);
     if (task == 0 && tiles_of(1) > 0) prefetch(1);
     if (need > 0) {
       // O goes through the wave's own LDS rows so that each global store
