@@ -99,7 +99,24 @@ sattn_mat_scores_kernel(const half_t* __restrict__ Q, const half_t* __restrict__
     acc = mfma(a, b, acc);
   }
   // element r of lane (n, g): query i0 + 8(r/4) + 4g + r%4, key jb
-  if (jb < T) {
+  if (j0 + 31 < i0 && j0 + 32 <= T && (T & 3) == 0 && (reinterpret_cast<uintptr_t>(S) & 15) == 0) {
+    // wholly below the diagonal, all 32 keys inside T: the block goes
+    // through the wave's LDS rows so that each store writes 16 bytes a lane,
+    // eight whole 128-byte rows an instruction
+    __shared__ __attribute__((aligned(16))) float blk[4][32 * 36];
+    float* const bw = blk[wave];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bw[(8 * (r >> 2) + 4 * g + (r & 3)) * 36 + n] = acc[r] * c;
+    const int rr = lane >> 3, ch = lane & 7;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {  // rows 8p + lane/8, keys 4(lane%8) .. +3
+      const int r = 8 * p + rr;
+      const float4v v = *reinterpret_cast<const float4v*>(bw + r * 36 + 4 * ch);
+      if (i0 + r < T)
+        __builtin_nontemporal_store(
+            v, reinterpret_cast<float4v*>(S + (size_t)h * T * T + (size_t)(i0 + r) * T + j0 + 4 * ch));
+    }
+  } else if (jb < T) {
     float* col = S + (size_t)h * T * T + jb;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
