@@ -73,12 +73,15 @@ def attention_ref(Q, K, Vt, c, *, heads=None, block: int = 256):
     return O, L
 
 
-def attention_rows_ref(Q, K, Vt, c, h: int, rows):
+def attention_rows_ref(Q, K, Vt, c, h: int, rows, *, key_chunk: int | None = None):
     """The same definition for selected rows of one query head.
 
     Returns ``(O_rows, L_rows)``: float64 ``[len(rows)][64]`` and
     ``[len(rows)]``; used to check sampled outputs at sizes where the full
-    oracle would take too long.
+    oracle would take too long.  With ``key_chunk``, the float64 copies of K
+    and V are made ``key_chunk`` keys at a time (the scores of every key are
+    still formed before the row's maximum and sum are taken), so rows with
+    millions of visible keys fit in memory; the arithmetic is unchanged.
     """
     Q, K, Vt, Hq, Hkv, T = _check(Q, K, Vt)
     kv = h // (Hq // Hkv)
@@ -86,14 +89,35 @@ def attention_rows_ref(Q, K, Vt, c, h: int, rows):
     rows = list(rows)
     O = np.empty((len(rows), HEAD_DIM))
     L = np.empty(len(rows))
-    for n, i in enumerate(rows):
-        q = Q[h, i].astype(np.float64)
-        t = (K[kv, :i + 1].astype(np.float64) @ q) * c
-        M = t.max()
-        w = np.exp2(t - M)
-        Z = w.sum()
-        O[n] = (Vt[kv, :, :i + 1].astype(np.float64) @ w) / Z
-        L[n] = M + np.log2(Z)
+    if key_chunk is None:
+        for n, i in enumerate(rows):
+            q = Q[h, i].astype(np.float64)
+            t = (K[kv, :i + 1].astype(np.float64) @ q) * c
+            M = t.max()
+            w = np.exp2(t - M)
+            Z = w.sum()
+            O[n] = (Vt[kv, :, :i + 1].astype(np.float64) @ w) / Z
+            L[n] = M + np.log2(Z)
+        return O, L
+    if len(rows) == 0:
+        return O, L
+    n_keys = max(rows) + 1
+    q = Q[h, rows].astype(np.float64)                       # [R][64]
+    t = np.empty((len(rows), n_keys))
+    for a in range(0, n_keys, key_chunk):
+        b = min(n_keys, a + key_chunk)
+        t[:, a:b] = (q @ K[kv, a:b].astype(np.float64).T) * c
+    t[np.arange(n_keys)[None, :] > np.asarray(rows)[:, None]] = -np.inf   # keys j <= i only
+    M = t.max(axis=1, keepdims=True)
+    w = np.exp2(t - M)
+    del t
+    Z = w.sum(axis=1)
+    acc = np.zeros((len(rows), HEAD_DIM))
+    for a in range(0, n_keys, key_chunk):
+        b = min(n_keys, a + key_chunk)
+        acc += w[:, a:b] @ Vt[kv, :, a:b].astype(np.float64).T
+    O[:] = acc / Z[:, None]
+    L[:] = M[:, 0] + np.log2(Z)
     return O, L
 
 

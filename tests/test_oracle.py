@@ -268,11 +268,26 @@ def test_rows_ref_agrees_with_full():
 
 def test_rows_ref_brute_force():
     x = make_inputs(6, 2, 1, seed=25)
-    Or, Lr = attention_rows_ref(x.Q, x.K, x.Vt, x.c, 1, range(6))
-    for i in range(6):
-        o, l = _decimal_row(x.Q, x.K, x.Vt, x.c, 1, i, 2)
-        assert np.allclose(Or[i], o, rtol=0, atol=1e-12)
-        assert abs(Lr[i] - l) <= 1e-12
+    for chunk in (None, 1, 4):
+        Or, Lr = attention_rows_ref(x.Q, x.K, x.Vt, x.c, 1, range(6), key_chunk=chunk)
+        for i in range(6):
+            o, l = _decimal_row(x.Q, x.K, x.Vt, x.c, 1, i, 2)
+            assert np.allclose(Or[i], o, rtol=0, atol=1e-12)
+            assert abs(Lr[i] - l) <= 1e-12
+
+
+def test_rows_ref_key_chunks_agree_with_full():
+    """The key-chunked evaluation (for rows with millions of keys) against the
+    full oracle, with chunk sizes that do and do not divide the key ranges, and
+    rows given out of order."""
+    x = make_inputs(300, 4, 2, seed=28, qk_std=1.5)
+    O, L = attention_ref(x.Q, x.K, x.Vt, x.c)
+    rows = [299, 0, 64, 63, 1, 200]
+    for chunk in (1, 7, 64, 100, 1000):
+        for h in (1, 2):
+            Or, Lr = attention_rows_ref(x.Q, x.K, x.Vt, x.c, h, rows, key_chunk=chunk)
+            assert np.allclose(Or, O[rows, h * 64:(h + 1) * 64], rtol=0, atol=1e-12)
+            assert np.allclose(Lr, L[h, rows], rtol=0, atol=1e-12)
 
 
 # --------------------------------------------------------------------------
