@@ -6,6 +6,11 @@ line: causal TFLOP/s (4*T^2*64*Hq/2 flop per call), the roofline of the
 kernel against the fp16 dense MFMA peak, and the float64 CPU oracle timed on
 a bounded sample of the same workload.
 
+Warm-up: the --warmup calls, continued until at least --min-warmup-s seconds
+of back-to-back calls have run (the card takes some load to reach its working
+clock); the line gives the warm-up's own call count and duration.  Then
+exactly --steps calls are timed.
+
 After the timed region the kernel runs back-to-back for about two seconds
 while a host thread reads the shader clock and socket power through amdsmi;
 the line's "clock" object gives them and the fraction of the fp16 peak
@@ -33,6 +38,7 @@ PEAK_FP16_TFLOPS = 2516.6  # MI355X dense fp16 MFMA: 256 CU x 2.4 GHz x 4096 flo
 WORKLOAD_INDEX = 3
 KERNEL_SRC = os.path.join(ROOT, "causal_attention_forward_amd", "csrc", "sattn_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sattn_fwd_T4096_Hq32_Hkv8.txt")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_sattn_fwd_T4096_Hq32_Hkv8.txt")
 BWD_KERNEL_SRC = os.path.join(ROOT, "causal_attention_forward_amd", "csrc", "sattn_bwd.hip")
 BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sattn_bwd_T4096_Hq32_Hkv8.txt")
 
@@ -52,9 +58,9 @@ def kernel_sha(src=KERNEL_SRC):
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def measured_traffic(path=TRAFFIC_FILE, src=KERNEL_SRC):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, or
-    None when it is missing or was taken on a different kernel source."""
+def counter_summary(path, src):
+    """The key: value lines of a committed rocprofv3 counter summary, or None
+    when it is missing or was taken on a different kernel source."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -64,31 +70,97 @@ def measured_traffic(path=TRAFFIC_FILE, src=KERNEL_SRC):
             kv[k.strip()] = v.strip()
     if kv.get("kernel_sha") != kernel_sha(src):
         return None
+    return kv
+
+
+def measured_traffic(path=TRAFFIC_FILE, src=KERNEL_SRC):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or
+    None when it is missing or was taken on a different kernel source."""
+    kv = counter_summary(path, src)
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv["hbm_bytes_per_launch"]) if kv else None
     except (KeyError, ValueError):
         return None
+
+
+def measured_utilisation(path=COUNTERS_FILE, src=KERNEL_SRC):
+    """Matrix-core and VALU utilisation of the kernel from a committed
+    rocprofv3 SQ-counter summary (fractions of the SIMD-cycles of a
+    dispatch), or None when missing or taken on a different kernel source."""
+    kv = counter_summary(path, src)
+    if not kv:
+        return None
+    try:
+        return {"mfma_busy": float(kv["mfma_busy"]), "valu_active": float(kv["valu_active"]),
+                "mfma_valu_coexec": float(kv["mfma_valu_coexec"]),
+                "wait_any": float(kv["wait_any"]),
+                "source": os.path.relpath(path, ROOT)}
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def blas_threads():
+    """Threads for the oracle's BLAS calls: the CPUs this process may run on
+    (its affinity mask), capped by OMP_NUM_THREADS where the host sets one
+    (the share of a shared host this process is meant to use)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        cap = 0
+    return (min(n, cap) if cap > 0 else n), n
+
+
+def timed_oracle(run_one, units, budget_s):
+    """Run `run_one(u)` for u = 0, 1, ... until `units` or about budget_s
+    seconds, with BLAS limited to blas_threads(); returns (done, seconds,
+    host facts)."""
+    threads, affinity = blas_threads()
+    facts = {"cores": threads, "affinity_cpus": affinity, "cpu_model": cpu_model(),
+             "threads_note": "BLAS products on `cores` threads; NumPy's exp2, max and "
+                             "sums run on one thread"}
+    import contextlib
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limits = threadpool_limits(limits=threads)
+    except Exception:
+        threadpool_info, limits = None, contextlib.nullcontext()
+    with limits:
+        t0 = time.perf_counter()
+        done = 0
+        while done < units:
+            run_one(done)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        if threadpool_info is not None:
+            used = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+            if used:
+                facts["cores"] = int(max(used))
+    return done, dt, facts
 
 
 def cpu_baseline(x, budget_s=20.0):
     """The float64 oracle on whole heads of the same workload, as many as fit
     in about budget_s seconds (at least one), scaled to TFLOP/s."""
     from oracle import attention_ref
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
-    t0 = time.perf_counter()
-    heads = 0
-    while heads < x.Hq:
-        attention_ref(x.Q, x.K, x.Vt, x.c, heads=[heads])
-        heads += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
+    heads, dt, facts = timed_oracle(
+        lambda h: attention_ref(x.Q, x.K, x.Vt, x.c, heads=[h]), x.Hq, budget_s)
     flops = causal_flops(x.T, 1) * heads
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "kind": "oracle", **facts,
             "sample": f"{heads} of {x.Hq} query heads of T={x.T} Hq={x.Hq} Hkv={x.Hkv} "
                       f"({dt:.1f} s, float64 NumPy)"}
 
@@ -166,6 +238,26 @@ def clock_fields(clock, achieved):
     return {**clock, "peak_at_clock": round(peak, 1), "frac_at_clock": round(achieved / peak, 4)}
 
 
+def warm_up(torch, step, calls, min_seconds):
+    """`calls` untimed calls, continued (in groups of ten) until at least
+    `min_seconds` of back-to-back work has run: the card raises its shader
+    clock over the first milliseconds of load, so a few calls alone leave the
+    timed region partly at a lower clock.  Returns the warm-up's calls and
+    seconds."""
+    t0 = time.perf_counter()
+    n = 0
+    for _ in range(calls):
+        step()
+        n += 1
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < min_seconds:
+        for _ in range(10):
+            step()
+            n += 1
+        torch.cuda.synchronize()
+    return n, time.perf_counter() - t0
+
+
 def backward_flops(T, Hq, d=64):
     """S, dP, dQ, dK and dV, each 2*64 flop per causal (query, key) pair."""
     return 2.5 * causal_flops(T, Hq, d)
@@ -175,25 +267,17 @@ def cpu_baseline_backward(x, dO, O, L, s, budget_s=20.0):
     """The float64 backward oracle on whole query heads (each with its own
     K/V head), as many as fit in about budget_s seconds, scaled to TFLOP/s."""
     from oracle import attention_backward_ref
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
     G = x.Hq // x.Hkv
-    t0 = time.perf_counter()
-    heads = 0
-    while heads < x.Hq:
-        h, kv = heads, heads // G
+
+    def one(h):
+        kv = h // G
         cols = slice(h * 64, (h + 1) * 64)
         attention_backward_ref(x.Q[h:h + 1], x.K[kv:kv + 1], x.Vt[kv:kv + 1], O[:, cols],
                                dO[:, cols], L[h:h + 1], x.c, s)
-        heads += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
+
+    heads, dt, facts = timed_oracle(one, x.Hq, budget_s)
     flops = backward_flops(x.T, 1) * heads
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "kind": "oracle", **facts,
             "sample": f"backward of {heads} of {x.Hq} query heads of T={x.T} Hq={x.Hq} "
                       f"Hkv={x.Hkv} ({dt:.1f} s, float64 NumPy)"}
 
@@ -245,9 +329,7 @@ def bench_backward(args, torch, sattn, x, w):
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / n
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_calls, warm_s = warm_up(torch, step, args.warmup, args.min_warmup_s)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
@@ -271,6 +353,8 @@ def bench_backward(args, torch, sattn, x, w):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_calls": warm_calls,
+        "warmup_s": round(warm_s, 3),
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -334,9 +418,7 @@ def bench_materialized(args, torch, sattn, x, w):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_calls, warm_s = warm_up(torch, step, args.warmup, args.min_warmup_s)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
@@ -376,6 +458,8 @@ def bench_materialized(args, torch, sattn, x, w):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_calls": warm_calls,
+        "warmup_s": round(warm_s, 3),
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -566,7 +650,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=300,
-                    help="untimed calls first; the GPU needs a few tens of ms of load to reach its working clock")
+                    help="untimed calls first (continued up to --min-warmup-s)")
+    ap.add_argument("--min-warmup-s", type=float, default=0.5,
+                    help="the warm-up runs at least this long: the GPU needs some load to reach "
+                         "its working clock")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the shader-clock window (amdsmi) after the timed region")
@@ -660,9 +747,7 @@ def main():
         def step():
             sattn.fwd(q, k, vt, x.c, out=O, lse=L, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_calls, warm_s = warm_up(torch, step, args.warmup, args.min_warmup_s)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -682,6 +767,7 @@ def main():
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     # the counter summary covers the default workload only
     traffic = None if args.vrows or args.workload != WORKLOAD_INDEX else measured_traffic()
+    utilisation = None if args.vrows or args.workload != WORKLOAD_INDEX else measured_utilisation()
     shape = f"T={x.T} Hq={x.Hq} Hkv={x.Hkv} d=64"
     out = {
         "metric": (f"causal attn fwd (V as rows) TFLOP/s, {shape}" if args.vrows else
@@ -691,6 +777,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_calls": warm_calls,
+        "warmup_s": round(warm_s, 3),
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -702,7 +790,8 @@ def main():
                    "pct_fp16_peak": round(100 * value / PEAK_FP16_TFLOPS, 2), **extra},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
-                     "traffic": traffic, "kernel_ms": round(kernel_ms, 5)},
+                     "traffic": traffic, "kernel_ms": round(kernel_ms, 5),
+                     "counters": utilisation},
     }
     if not args.no_clock:
         out["clock"] = clock_fields(gfx_clock_window(torch, step), achieved)

@@ -36,7 +36,8 @@
 //    and 5 LDS buffers (101 KiB).
 //    Global loads run one stage (two steps) ahead of their LDS stores through
 //    registers, and every stage issues the same loads (tiles past the end
-//    read as zeros through buffer-descriptor range checks), so the waits on
+//    read as zeros through buffer-descriptor range checks, applied to the
+//    loads' VGPR offsets, which carry the whole offset), so the waits on
 //    them stay exact.  LDS rows are padded to 144 bytes so the 16-byte
 //    operand reads of 16 lanes hit 64 distinct banks.
 //  * The reference maximum is moved lazily.  P is formed against the current
@@ -127,6 +128,16 @@ __device__ __forceinline__ float sum32(const float16v& a, const float16v& b) {
 // flight across it are not waited for.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Orders a wave's LDS writes before its reads of what other lanes of the
+// same wave wrote (wavefront-scope release, wave barrier, acquire).  A wave's
+// LDS operations complete in order, so this emits no wait; it keeps the
+// compiler from moving the reads above the writes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // The value held by the lane whose byte address (lane index * 4) is `addr`.
 __device__ __forceinline__ float xlane(float x, int addr) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, x)));
@@ -177,7 +188,7 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
   constexpr int kKRing = 6;                // K tile t is read at steps t-1 and t
   constexpr int kVRing = 5;                // V^T tile t is read at step t+1
   constexpr float kSumCap = 256.0f;        // 2^kLazy
-  constexpr int kOutOfRange = 0x7FFFFFF0;  // a buffer offset past every range
+  constexpr unsigned kOutOfRange = 0x7FFFFFF0u;  // past every plane (at most 2^31 - 128 bytes)
   __shared__ __attribute__((aligned(16))) half_t smem[(kKRing + kVRing) * kTileHalfs];
   // each wave's 32 O rows on their way to global memory (see the epilogue)
   __shared__ __attribute__((aligned(16))) half_t obuf[kNW][32 * kRowHalfs];
@@ -230,14 +241,19 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
   const __amdgpu_buffer_rsrc_t vrsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(Vh), 0, kD * T * 2, kBufferWord3);
   const int kByte = (cr * kD + cc * 8) * 2;
-  const int vByte = (cr * T + cc * 8) * 2;
+  const unsigned vByte = ((unsigned)cr * (unsigned)T + (unsigned)cc * 8u) * 2u;
   typedef int4v Stage[kCpt];
+  // The whole offset of every buffer load is in its VGPR offset, which the
+  // range check covers (the scalar offset is added after the check): rows
+  // past T, and whole tiles past the last, read as zeros without touching
+  // memory past the head's plane.  Offsets stay below 2^31 + 2^15 for every
+  // admitted shape (a plane holds at most 2^31 bytes), so they are unsigned.
   auto load_k = [&](int kt, Stage& dst) {
+    const unsigned t0 = (unsigned)__builtin_amdgcn_readfirstlane(kt) * (unsigned)(kBN * kD * 2);
 #pragma unroll
     for (int p = 0; p < kCpt; ++p)
       dst[p] = __builtin_amdgcn_raw_buffer_load_b128(
-          krsrc, kByte + p * kRowsPerPass * kD * 2,
-          __builtin_amdgcn_readfirstlane(kt * kBN * kD * 2), 0);
+          krsrc, t0 + (unsigned)(kByte + p * kRowsPerPass * kD * 2), 0, 0);
   };
   // V^T chunks at or past T (T % 8 == 0: a chunk is wholly inside or
   // outside) take an offset past the buffer's range and read as zeros, so
@@ -246,17 +262,16 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
     const int key0 = kt * kBN;
 #pragma unroll
     for (int p = 0; p < kCpt; ++p) {
-      const int rb = vByte + p * kRowsPerPass * T * 2;
+      const unsigned rb = (unsigned)vByte + (unsigned)(p * kRowsPerPass) * (unsigned)T * 2u;
       if (VROWS) {  // rows past T read as zeros, like K's
+        const unsigned t0 = (unsigned)__builtin_amdgcn_readfirstlane(kt) * (unsigned)(kBN * kD * 2);
         dst[p] = __builtin_amdgcn_raw_buffer_load_b128(
-            vrsrc, kByte + p * kRowsPerPass * kD * 2,
-            __builtin_amdgcn_readfirstlane(kt * kBN * kD * 2), 0);
+            vrsrc, t0 + (unsigned)(kByte + p * kRowsPerPass * kD * 2), 0, 0);
       } else if (VT_VEC) {
-        const int off = key0 + cc * 8 < T ? rb : kOutOfRange;
-        dst[p] = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off,
-                                                       __builtin_amdgcn_readfirstlane(key0 * 2), 0);
+        const unsigned off = key0 + cc * 8 < T ? rb + (unsigned)key0 * 2u : (unsigned)kOutOfRange;
+        dst[p] = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off, 0, 0);
       } else if (key0 + kBN <= T) {
-        dst[p] = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, rb, key0 * 2, 0);
+        dst[p] = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, rb + (unsigned)key0 * 2u, 0, 0);
       } else {
         const half_t* vsrc = Vh + (size_t)(cr + p * kRowsPerPass) * T + key0 + cc * 8;
         half8 v;
@@ -604,7 +619,7 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
       // writes whole 128-byte row segments (eight lanes a row) rather than
       // 8 bytes in each of 32 rows.  Accumulator element 4 q4 + e of lane
       // (n, g) is d = 8 q4 + 4 g + e (o1: d + 32) of row n.  The wave reads
-      // back only what it wrote, and a wave's LDS accesses complete in order.
+      // back only what its own lanes wrote.
       half_t* const ob = obuf[wave];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -614,6 +629,7 @@ sattn_fwd_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
         *reinterpret_cast<half4*>(orow) = __builtin_convertvector(va * inv, half4);
         *reinterpret_cast<half4*>(orow + 32) = __builtin_convertvector(vb * inv, half4);
       }
+      wave_lds_sync();
       const int row0 = 32 * blk, rr = lane >> 3, ch = lane & 7;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {  // rows 8p + lane/8, 16-byte chunk lane%8

@@ -107,6 +107,11 @@ sattn_mat_scores_kernel(const half_t* __restrict__ Q, const half_t* __restrict__
     float* const bw = blk[wave];
 #pragma unroll
     for (int r = 0; r < 16; ++r) bw[(8 * (r >> 2) + 4 * g + (r & 3)) * 36 + n] = acc[r] * c;
+    // other lanes of this wave read what these wrote: order the LDS accesses
+    // (a wave's LDS operations complete in order, so this emits no wait)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int rr = lane >> 3, ch = lane & 7;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {  // rows 8p + lane/8, keys 4(lane%8) .. +3

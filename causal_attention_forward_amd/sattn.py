@@ -130,24 +130,48 @@ def sattn_fwd_check(Q: int, K: int, Vt: int, O: int, L: int, c: float, T: int, H
     return _lib.sattn_fwd_check(Q, K, Vt, O, L, ctypes.c_float(c), T, Hq, Hkv)
 
 
+def _check_tensor(name, x, dtype, shape, device):
+    """x must be a contiguous `dtype` tensor of `shape` on the GPU `device`:
+    the library reads and writes through the raw address, so anything else
+    would make the kernels touch memory that is not the tensor's."""
+    import torch
+    if not isinstance(x, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if (tuple(x.shape) != tuple(shape) or x.dtype != dtype or not x.is_cuda
+            or not x.is_contiguous() or (device is not None and x.device != device)):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                         f"on {device if device is not None else 'the GPU'} (got "
+                         f"{x.dtype} {tuple(x.shape)} on {x.device}, "
+                         f"contiguous={x.is_contiguous()})")
+
+
+def _fwd_operands(q, k, v, v_shape_of, out, lse):
+    """Checks of the forward's operands; allocates O and L when not given."""
+    import torch
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a float16 GPU tensor [Hq][T][64]")
+    Hq, T, D = q.shape
+    if not isinstance(k, torch.Tensor) or k.dim() != 3:
+        raise ValueError("k must be a float16 GPU tensor [Hkv][T][64]")
+    Hkv = k.shape[0]
+    dev = q.device
+    _check_tensor("q", q, torch.float16, (Hq, T, HEAD_DIM), None)
+    _check_tensor("k", k, torch.float16, (Hkv, T, HEAD_DIM), dev)
+    _check_tensor("v", v, torch.float16, v_shape_of(Hkv, T), dev)
+    if out is None:
+        out = torch.empty((T, Hq * D), dtype=torch.float16, device=dev)
+    if lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    _check_tensor("out", out, torch.float16, (T, Hq * HEAD_DIM), dev)
+    _check_tensor("lse", lse, torch.float32, (Hq, T), dev)
+    return Hq, T, Hkv, out, lse
+
+
 def fwd_vrows(q, k, v, c, out=None, lse=None, stream=None):
     """As ``fwd`` with V given as rows: v float16 [Hkv][T][64] (no V^T needed)."""
     import torch
 
-    Hq, T, D = q.shape
-    Hkv = k.shape[0]
-    if D != HEAD_DIM or tuple(k.shape) != (Hkv, T, D) or tuple(v.shape) != (Hkv, T, D):
-        raise ValueError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
-    for name, x in (("q", q), ("k", k), ("v", v)):
-        if x.dtype != torch.float16 or not x.is_cuda or not x.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous float16 GPU tensor")
-    if out is None:
-        out = torch.empty((T, Hq * D), dtype=torch.float16, device=q.device)
-    if lse is None:
-        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
-    if (out.dtype != torch.float16 or lse.dtype != torch.float32 or not out.is_contiguous()
-            or not lse.is_contiguous() or out.numel() != T * Hq * D or lse.numel() != Hq * T):
-        raise ValueError("out must be contiguous float16 [T][Hq*64], lse contiguous float32 [Hq][T]")
+    Hq, T, Hkv, out, lse = _fwd_operands(q, k, v, lambda hkv, t: (hkv, t, HEAD_DIM), out, lse)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     with torch.cuda.device(q.device):
@@ -168,20 +192,7 @@ def fwd(q, k, vt, c, out=None, lse=None, stream=None):
     """
     import torch
 
-    Hq, T, D = q.shape
-    Hkv = k.shape[0]
-    if D != HEAD_DIM or tuple(k.shape) != (Hkv, T, D) or tuple(vt.shape) != (Hkv, D, T):
-        raise ValueError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} vt{tuple(vt.shape)}")
-    for name, x in (("q", q), ("k", k), ("vt", vt)):
-        if x.dtype != torch.float16 or not x.is_cuda or not x.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous float16 GPU tensor")
-    if out is None:
-        out = torch.empty((T, Hq * D), dtype=torch.float16, device=q.device)
-    if lse is None:
-        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
-    if (out.dtype != torch.float16 or lse.dtype != torch.float32 or not out.is_contiguous()
-            or not lse.is_contiguous() or out.numel() != T * Hq * D or lse.numel() != Hq * T):
-        raise ValueError("out must be contiguous float16 [T][Hq*64], lse contiguous float32 [Hq][T]")
+    Hq, T, Hkv, out, lse = _fwd_operands(q, k, vt, lambda hkv, t: (hkv, HEAD_DIM, t), out, lse)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     with torch.cuda.device(q.device):
@@ -233,19 +244,11 @@ def sattn_bwd_key(Q, K, Vt, dO, L, D, dK, dVt, ws, ws_bytes, c, s, T, Hq, Hkv,
                               ctypes.c_float(s), T, Hq, Hkv, stream)
 
 
-def _check_half(name, x, shape):
-    import torch
-    if tuple(x.shape) != tuple(shape) or x.dtype != torch.float16 or not x.is_cuda \
-            or not x.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous float16 GPU tensor of shape {tuple(shape)}")
-
-
 def _out(x, shape, dev):
     import torch
     if x is None:
         return torch.empty(shape, dtype=torch.float32, device=dev)
-    if tuple(x.shape) != tuple(shape) or x.dtype != torch.float32 or not x.is_contiguous():
-        raise ValueError(f"outputs must be contiguous float32 of shape {tuple(shape)}")
+    _check_tensor("output", x, torch.float32, shape, dev)
     return x
 
 
@@ -262,16 +265,19 @@ def bwd(q, k, vt, o, do, lse, c, s, dq=None, dk=None, dvt=None, D=None, workspac
     allocated here unless given.
     """
     import torch
+    if not isinstance(q, torch.Tensor) or q.dim() != 3 or not isinstance(k, torch.Tensor) \
+            or k.dim() != 3:
+        raise ValueError("q [Hq][T][64] and k [Hkv][T][64] must be float16 GPU tensors")
     Hq, T, _ = q.shape
     Hkv = k.shape[0]
-    _check_half("q", q, (Hq, T, HEAD_DIM))
-    _check_half("k", k, (Hkv, T, HEAD_DIM))
-    _check_half("vt", vt, (Hkv, HEAD_DIM, T))
-    _check_half("o", o, (T, Hq * HEAD_DIM))
-    _check_half("do", do, (T, Hq * HEAD_DIM))
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, T) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [Hq][T]")
     dev = q.device
+    f16, f32 = torch.float16, torch.float32
+    _check_tensor("q", q, f16, (Hq, T, HEAD_DIM), None)
+    _check_tensor("k", k, f16, (Hkv, T, HEAD_DIM), dev)
+    _check_tensor("vt", vt, f16, (Hkv, HEAD_DIM, T), dev)
+    _check_tensor("o", o, f16, (T, Hq * HEAD_DIM), dev)
+    _check_tensor("do", do, f16, (T, Hq * HEAD_DIM), dev)
+    _check_tensor("lse", lse, f32, (Hq, T), dev)
     dq = _out(dq, (Hq, T, HEAD_DIM), dev)
     dk = _out(dk, (Hkv, T, HEAD_DIM), dev)
     dvt = _out(dvt, (Hkv, HEAD_DIM, T), dev)
@@ -279,6 +285,10 @@ def bwd(q, k, vt, o, do, lse, c, s, dq=None, dk=None, dvt=None, D=None, workspac
     need = sattn_bwd_workspace_bytes(T, Hq, Hkv)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda \
+                or workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError(f"workspace must be a contiguous tensor on {dev}")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if stream is None:
@@ -334,22 +344,18 @@ def mat_fwd(q, k, vt, c, scores=None, probs=None, out=None, lse=None, stream=Non
 
     Returns ``(O, L, S, P)``: float16 [T][Hq*64], float32 [Hq][T], and the
     planes float32 / float16 [Hq][T][T] (entries above the diagonal are left
-    as allocated).
+    as allocated).  Caller-given planes and outputs must be contiguous, of
+    those dtypes and shapes, on q's device.
     """
     import torch
-    Hq, T, D = q.shape
-    Hkv = k.shape[0]
-    if D != HEAD_DIM or tuple(k.shape) != (Hkv, T, D) or tuple(vt.shape) != (Hkv, D, T):
-        raise ValueError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} vt{tuple(vt.shape)}")
+    Hq, T, Hkv, out, lse = _fwd_operands(q, k, vt, lambda hkv, t: (hkv, HEAD_DIM, t), out, lse)
     dev = q.device
     if scores is None:
         scores = torch.empty((Hq, T, T), dtype=torch.float32, device=dev)
     if probs is None:
         probs = torch.empty((Hq, T, T), dtype=torch.float16, device=dev)
-    if out is None:
-        out = torch.empty((T, Hq * D), dtype=torch.float16, device=dev)
-    if lse is None:
-        lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    _check_tensor("scores", scores, torch.float32, (Hq, T, T), dev)
+    _check_tensor("probs", probs, torch.float16, (Hq, T, T), dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):

@@ -79,10 +79,12 @@ int sattn_fwd(const void* Q, const void* K, const void* Vt, void* O, float* L,
  * (V of K/V head kv, token j at (kv*T + j)*64), the layout the value
  * projection produces, instead of V^T; everything else, the results
  * included, is as for sattn_fwd (bit-identical O and L for the same values).
- * It removes the value-transpose step before the attention (StreamingAttention
- * head-layout page, value-transpose; Graph page, cgLayerForwardWith): the
- * kernel reads the V^T operand of P V from row-major V tiles with the gfx950
- * LDS transpose read.  V must be 16-byte aligned; validation as sattn_fwd.
+ * It removes the value-transpose step before the attention (the Graph page's
+ * cgLayerForwardWith launches the value-transpose image on the layer's QKV
+ * plane before the attention; the DeviceImages page lists that image in
+ * coppeliusCoreDeviceImages): the kernel reads the V^T operand of P V from
+ * row-major V tiles with the gfx950 LDS transpose read.  V must be 16-byte
+ * aligned; validation as sattn_fwd.
  */
 int sattn_fwd_vrows(const void* Q, const void* K, const void* V, void* O, float* L, float c,
                     int T, int Hq, int Hkv, void* stream);

@@ -36,6 +36,12 @@ def test_traffic_summary_matches_the_kernel_source():
     assert 42467328 <= got <= 1.05 * 42467328
 
 
+def test_counter_summary_matches_the_kernel_source():
+    got = bench.measured_utilisation()
+    assert got is not None, "profiles/ SQ counter summary is stale or missing"
+    assert 0.0 < got["mfma_busy"] < 1.0 and 0.0 < got["valu_active"] < 1.0
+
+
 def test_backward_traffic_summary_matches_the_kernel_source():
     got = bench.measured_traffic(bench.BWD_TRAFFIC_FILE, bench.BWD_KERNEL_SRC)
     assert got is not None, "profiles/ backward traffic summary is stale or missing"

@@ -1,7 +1,10 @@
 """The largest admitted problem: Hq * 64 * T * 4 <= 2^32 - 1 (the admission
 rule), here T = 131071 (ragged: not a multiple of 64) with Hq = 128, Hkv = 8,
-just under the bound (2^32 - 2^15).  The 32-bit offsets of the buffer loads
-and the output planes reach their largest values.
+just under the bound (2^32 - 2^15).  The whole-tensor sizes reach their
+largest values: O and the forward's Q planes hold 2^31 - 2^14 bytes, the
+backward's binary32 dQ 2^32 - 2^15, so every offset into them past 2^31 is
+taken.  (The per-head buffer offsets scale with T alone and peak at Hq = 1
+with the largest T; test_parity_main covers that case.)
 
 Inputs: one head of Q, K, V, dO (and O) is drawn at full length from the
 seeded generator; the other heads are distinct cyclic shifts of it along the
