@@ -13,6 +13,7 @@
 #include <stdint.h>
 
 #include "sattn.h"
+#include "sattn_check.h"
 
 namespace {
 
@@ -72,6 +73,9 @@ struct BwdArgs {
   unsigned long long wsBytes;
   float c, s;
   int T, Hq, Hkv;
+  // nonzero: the workspace is the library's own static region of this many
+  // bytes (ws is ignored; it cannot overlap caller buffers)
+  unsigned long long libWsBytes = 0;
 };
 
 int check_bwd(const BwdArgs& a, bool query, bool key) {
@@ -83,14 +87,16 @@ int check_bwd(const BwdArgs& a, bool query, bool key) {
   if (st != SATTN_OK) return st;
   if (!isfinite(a.s) || !(a.s > 0.0f)) return SATTN_ERR_SCALE;
   const unsigned long long need = sattn_bwd_workspace_bytes(a.T, a.Hq, a.Hkv);
-  if (key && need > 0 && (!a.ws || a.wsBytes < need)) return SATTN_ERR_WORKSPACE;
+  if (key && need > 0 && a.libWsBytes > 0 && need > a.libWsBytes) return SATTN_ERR_SCRATCH;
+  if (key && need > 0 && a.libWsBytes == 0 && (!a.ws || a.wsBytes < need))
+    return SATTN_ERR_WORKSPACE;
   if (misaligned(a.Q, 16) || misaligned(a.K, 16) || misaligned(a.Vt, 16) ||
       misaligned(a.dO, 16) || misaligned(a.L, 4))
     return SATTN_ERR_ALIGN;
   if (query && (misaligned(a.O, 16) || misaligned(a.dQ, 16) || misaligned(a.D_out, 4)))
     return SATTN_ERR_ALIGN;
-  if (key && (misaligned(a.dK, 16) || misaligned(a.dVt, 16) || misaligned(a.ws, 16) ||
-              misaligned(a.D_in, 4)))
+  if (key && (misaligned(a.dK, 16) || misaligned(a.dVt, 16) ||
+              (a.libWsBytes == 0 && misaligned(a.ws, 16)) || misaligned(a.D_in, 4)))
     return SATTN_ERR_ALIGN;
   const uint64_t t = static_cast<uint64_t>(a.T);
   const uint64_t hq = static_cast<uint64_t>(a.Hq), hkv = static_cast<uint64_t>(a.Hkv);
@@ -113,7 +119,7 @@ int check_bwd(const BwdArgs& a, bool query, bool key) {
   if (key) {
     out[nOut++] = span(a.dK, hkv * word);
     out[nOut++] = span(a.dVt, hkv * word);
-    if (need > 0) out[nOut++] = span(a.ws, need);
+    if (need > 0 && a.libWsBytes == 0) out[nOut++] = span(a.ws, need);
   }
   for (int i = 0; i < nOut; ++i) {
     for (int j = 0; j < nIn; ++j)
@@ -157,6 +163,18 @@ extern "C" int sattn_bwd_key_check(const void* Q, const void* K, const void* Vt,
                                    int Hq, int Hkv) {
   const BwdArgs a{Q, K, Vt, nullptr, dO, L, nullptr, nullptr, dK, dVt, workspace, D,
                   workspace_bytes, c, s, T, Hq, Hkv};
+  return check_bwd(a, false, true);
+}
+
+// The validation of sattn_bwd_key_noalloc: as sattn_bwd_key_check, with the
+// workspace replaced by the library's static region of `scratch_bytes`.
+int sattn_bwd_key_noalloc_check(const void* Q, const void* K, const void* Vt, const void* dO,
+                                const float* L, const float* D, const float* dK,
+                                const float* dVt, float c, float s, int T, int Hq, int Hkv,
+                                unsigned long long scratch_bytes) {
+  BwdArgs a{Q, K, Vt, nullptr, dO, L, nullptr, nullptr, dK, dVt, nullptr, D, 0,
+            c, s, T, Hq, Hkv};
+  a.libWsBytes = scratch_bytes;
   return check_bwd(a, false, true);
 }
 
@@ -262,6 +280,9 @@ extern "C" const char* sattn_status_string(int status) {
     case SATTN_ERR_DEVICE: return "no current HIP device, or it is not gfx950";
     case SATTN_ERR_LAUNCH: return "the kernel launch failed";
     case SATTN_ERR_WORKSPACE: return "the workspace is NULL or smaller than sattn_bwd_workspace_bytes()";
+    case SATTN_ERR_SCRATCH:
+      return "the problem needs more workspace than sattn_bwd_key_noalloc's static region "
+             "(SATTN_BWD_NOALLOC_MAX_BYTES)";
     default: return "unknown sattn status";
   }
 }

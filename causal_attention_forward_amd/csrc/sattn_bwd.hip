@@ -51,6 +51,7 @@
 #include <atomic>
 
 #include "sattn.h"
+#include "sattn_check.h"
 #include "sattn_lds.h"
 
 namespace {
@@ -1023,7 +1024,49 @@ void launch_key(const half_t* Q, const half_t* K, const half_t* Vt, const half_t
   }
 }
 
+// sattn_bwd_key_noalloc's workspace: one static region per GPU, loaded with
+// the library's code object.  In host code `scratch` names a host-side stand-in,
+// not the device region: its device address is taken with
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+constexpr unsigned long long kScratchBytes = SATTN_BWD_NOALLOC_MAX_BYTES;
+__device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+std::atomic<float*> g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (the device must be current), or
+// NULL if the runtime cannot give it.
+float* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  if (dev < kMaxDevices) {
+    float* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+  }
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+  if (dev < kMaxDevices) g_scratch_ptr[dev].store(static_cast<float*>(ptr), std::memory_order_release);
+  return static_cast<float*>(ptr);
+}
+
 }  // namespace
+
+extern "C" int sattn_bwd_key_noalloc(const void* Q, const void* K, const void* Vt, const void* dO,
+                                     const float* L, const float* D, float* dK, float* dVt,
+                                     float c, float s, int T, int Hq, int Hkv, void* stream) {
+  const int st = sattn_bwd_key_noalloc_check(Q, K, Vt, dO, L, D, dK, dVt, c, s, T, Hq, Hkv,
+                                             kScratchBytes);
+  if (st != SATTN_OK) return st;
+  const int dst = check_device();
+  if (dst != SATTN_OK) return dst;
+  float* ws = nullptr;
+  if (sattn_bwd_workspace_bytes(T, Hq, Hkv) > 0) {
+    ws = scratch_address();
+    if (ws == nullptr) return SATTN_ERR_DEVICE;
+  }
+  launch_key(static_cast<const half_t*>(Q), static_cast<const half_t*>(K),
+             static_cast<const half_t*>(Vt), static_cast<const half_t*>(dO), L, D, dK, dVt, ws,
+             c, s, T, Hq, Hkv, static_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? SATTN_OK : SATTN_ERR_LAUNCH;
+}
 
 extern "C" int sattn_bwd_query(const void* Q, const void* K, const void* Vt, const void* O,
                                const void* dO, const float* L, float* dQ, float* D, float c,

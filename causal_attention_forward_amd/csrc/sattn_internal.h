@@ -11,4 +11,6 @@
 void sattn_fwd_split_launch(const void* Q, const void* K, const void* V, void* O, float* L,
                             float c, int T, int Hq, int Hkv, bool vrows, hipStream_t stream);
 
+#include "sattn_check.h"
+
 #endif  // SATTN_INTERNAL_H

@@ -73,6 +73,8 @@ _lib.sattn_bwd_query.restype = ctypes.c_int
 _lib.sattn_bwd_query.argtypes = [_P] * 8 + [_F, _F, _I, _I, _I, _P]
 _lib.sattn_bwd_key.restype = ctypes.c_int
 _lib.sattn_bwd_key.argtypes = [_P] * 9 + [_U64, _F, _F, _I, _I, _I, _P]
+_lib.sattn_bwd_key_noalloc.restype = ctypes.c_int
+_lib.sattn_bwd_key_noalloc.argtypes = [_P] * 8 + [_F, _F, _I, _I, _I, _P]
 _lib.sattn_bwd.restype = ctypes.c_int
 _lib.sattn_bwd.argtypes = [_P] * 11 + [_U64, _F, _F, _I, _I, _I, _P]
 _lib.sattn_bwd_workspace_bytes.restype = ctypes.c_ulonglong
@@ -93,10 +95,13 @@ SATTN_ERR_ALIAS = 5
 SATTN_ERR_DEVICE = 6
 SATTN_ERR_LAUNCH = 7
 SATTN_ERR_WORKSPACE = 8
+SATTN_ERR_SCRATCH = 9
+BWD_NOALLOC_MAX_BYTES = 64 << 20   # SATTN_BWD_NOALLOC_MAX_BYTES
 HEAD_DIM = 64
 
 EXPORTS = ("sattn_fwd", "sattn_fwd_vrows", "sattn_fwd_check", "sattn_status_string", "sattn_bwd_query",
-           "sattn_bwd_key", "sattn_bwd", "sattn_bwd_workspace_bytes", "sattn_bwd_check",
+           "sattn_bwd_key", "sattn_bwd_key_noalloc", "sattn_bwd", "sattn_bwd_workspace_bytes",
+           "sattn_bwd_check",
            "sattn_bwd_query_check", "sattn_bwd_key_check", "sattn_mat_fwd",
            "sattn_mat_fwd_check", "sattn_mat_scores", "sattn_mat_softmax", "sattn_mat_pv",
            "sattn_mat_scores_check", "sattn_mat_softmax_check", "sattn_mat_pv_check")
@@ -242,6 +247,12 @@ def sattn_bwd_key(Q, K, Vt, dO, L, D, dK, dVt, ws, ws_bytes, c, s, T, Hq, Hkv,
                   stream=None) -> int:
     return _lib.sattn_bwd_key(Q, K, Vt, dO, L, D, dK, dVt, ws, ws_bytes, ctypes.c_float(c),
                               ctypes.c_float(s), T, Hq, Hkv, stream)
+
+
+def sattn_bwd_key_noalloc(Q, K, Vt, dO, L, D, dK, dVt, c, s, T, Hq, Hkv, stream=None) -> int:
+    """The key launch with the library's static workspace (allocates nothing)."""
+    return _lib.sattn_bwd_key_noalloc(Q, K, Vt, dO, L, D, dK, dVt, ctypes.c_float(c),
+                                      ctypes.c_float(s), T, Hq, Hkv, stream)
 
 
 def _out(x, shape, dev):

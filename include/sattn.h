@@ -19,7 +19,8 @@
  * it is 0x3E38AA3B (Graph page, cgStreamingScale).
  *
  * All functions are thread-safe.  No entry point allocates memory or keeps
- * state between calls besides a per-device cache of the architecture check.
+ * state between calls besides a per-device cache of the architecture check
+ * (and, for sattn_bwd_key_noalloc, of its static region's address).
  */
 #ifndef SATTN_H
 #define SATTN_H
@@ -40,7 +41,9 @@ typedef enum {
   SATTN_ERR_ALIAS = 5,  /* an output overlaps an input or another output              */
   SATTN_ERR_DEVICE = 6, /* no current HIP device, or it is not gfx950                 */
   SATTN_ERR_LAUNCH = 7, /* the kernel launch was refused (hipGetLastError)            */
-  SATTN_ERR_WORKSPACE = 8 /* the backward's workspace is NULL or smaller than needed   */
+  SATTN_ERR_WORKSPACE = 8, /* the backward's workspace is NULL or smaller than needed  */
+  SATTN_ERR_SCRATCH = 9    /* sattn_bwd_key_noalloc: the problem needs more workspace
+                              than its static region holds                            */
 } sattn_status;
 
 /*
@@ -162,6 +165,26 @@ int sattn_bwd_key(const void* Q, const void* K, const void* Vt, const void* dO,
                   const float* L, const float* D, float* dK, float* dVt, void* workspace,
                   unsigned long long workspace_bytes, float c, float s, int T, int Hq, int Hkv,
                   void* stream);
+
+/*
+ * sattn_bwd_key_noalloc: sattn_bwd_key for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the per-query-head planes that sattn_bwd_key keeps
+ * in the caller's workspace live instead in one static device region of the
+ * library, SATTN_BWD_NOALLOC_MAX_BYTES (64 MiB) on each GPU the library runs
+ * on, held until the process ends.  No call allocates or frees anything.
+ * Arguments, layouts, results (bit-identical to sattn_bwd_key's) and
+ * validation as sattn_bwd_key without the workspace; SATTN_ERR_SCRATCH when
+ * sattn_bwd_workspace_bytes(T, Hq, Hkv) exceeds SATTN_BWD_NOALLOC_MAX_BYTES
+ * (nothing is launched).  Every call on a GPU uses that GPU's one region:
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * on it and give wrong dK and dVt, so such calls must be ordered (one
+ * stream, or events).  The region's contents on entry do not matter.
+ */
+#define SATTN_BWD_NOALLOC_MAX_BYTES (64ull << 20)
+int sattn_bwd_key_noalloc(const void* Q, const void* K, const void* Vt, const void* dO,
+                          const float* L, const float* D, float* dK, float* dVt, float c,
+                          float s, int T, int Hq, int Hkv, void* stream);
 
 /*
  * sattn_bwd: sattn_bwd_query then sattn_bwd_key on `stream`; the outputs of

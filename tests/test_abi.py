@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "sattn_fwd", "sattn_fwd_vrows", "sattn_fwd_check", "sattn_status_string", "sattn_bwd",
         "sattn_bwd_check",
-        "sattn_bwd_key", "sattn_bwd_key_check", "sattn_bwd_query", "sattn_bwd_query_check",
+        "sattn_bwd_key", "sattn_bwd_key_check", "sattn_bwd_key_noalloc", "sattn_bwd_query",
+        "sattn_bwd_query_check",
         "sattn_bwd_workspace_bytes", "sattn_mat_fwd", "sattn_mat_fwd_check",
         "sattn_mat_scores", "sattn_mat_softmax", "sattn_mat_pv", "sattn_mat_scores_check",
         "sattn_mat_softmax_check", "sattn_mat_pv_check"])
@@ -46,10 +47,10 @@ def test_library_exports_every_declared_symbol(sattn):
 
 
 def test_status_strings(sattn):
-    for s in range(9):
+    for s in range(10):
         text = sattn.sattn_status_string(s)
         assert text and text != "unknown sattn status"
-    assert sattn.sattn_status_string(9) == "unknown sattn status"
+    assert sattn.sattn_status_string(10) == "unknown sattn status"
     assert sattn.sattn_status_string(-1) == "unknown sattn status"
 
 

@@ -103,3 +103,25 @@ def test_entry_points_validate_before_any_device_call(sattn):
     assert sattn.sattn_bwd_key(a["Q"], a["K"], a["Vt"], a["dO"], a["L"], a["D"], a["dK"],
                                a["dVt"], a["ws"], 16, C, S, T, HQ,
                                HKV) == sattn.SATTN_ERR_WORKSPACE
+
+
+def noalloc(sattn, t=T, hq=HQ, hkv=HKV, c=C, s=S, **kw):
+    a = {**A, **kw}
+    return sattn.sattn_bwd_key_noalloc(a["Q"], a["K"], a["Vt"], a["dO"], a["L"], a["D"], a["dK"],
+                                       a["dVt"], c, s, t, hq, hkv)
+
+
+def test_noalloc_key_launch_validates_before_any_device_call(sattn):
+    """sattn_bwd_key_noalloc rejects bad arguments as sattn_bwd_key does, and a
+    problem whose workspace exceeds its static region with SATTN_ERR_SCRATCH,
+    all before any HIP call (the addresses here are fake)."""
+    assert noalloc(sattn, D=None) == sattn.SATTN_ERR_NULL
+    assert noalloc(sattn, t=0) == sattn.SATTN_ERR_SHAPE
+    assert noalloc(sattn, c=math.nan) == sattn.SATTN_ERR_SCALE
+    assert noalloc(sattn, dK=A["dK"] + 4) == sattn.SATTN_ERR_ALIGN
+    assert noalloc(sattn, dVt=A["dK"]) == sattn.SATTN_ERR_ALIAS
+    limit = sattn.BWD_NOALLOC_MAX_BYTES
+    # T=4096 Hq=32 Hkv=8 needs exactly the region; one more token does not fit
+    assert need(4096, 32, 8) == limit
+    assert noalloc(sattn, t=4097, hq=32, hkv=8) == sattn.SATTN_ERR_SCRATCH
+    assert noalloc(sattn, t=1 << 20, hq=4, hkv=1) == sattn.SATTN_ERR_SCRATCH
