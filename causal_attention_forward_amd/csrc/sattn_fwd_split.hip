@@ -20,12 +20,19 @@
 //    has no barrier: a tile's K rows and V^T rows (or V rows) are read with
 //    fully coalesced 16-byte loads (eight whole 128-byte lines per
 //    instruction; rows and keys past T read as zeros through the buffer
-//    range checks), the next tile's loads in flight while the current one is
-//    computed, and stored swizzled so that the operand reads hit every bank
-//    once.  Given V as rows, the V^T operand comes from transpose reads of
-//    the V-rows tile.  (Operands loaded straight from global memory, as
+//    range checks) and stored swizzled so that the operand reads hit every
+//    bank once.  Given V as rows, the V^T operand comes from transpose reads
+//    of the V-rows tile.  (Operands loaded straight from global memory, as
 //    16-byte pieces of 32 different lines per instruction, left the CU's
 //    load path the bottleneck.)
+//  * Two ways of staging.  When the grid fits the chip in one wave of
+//    workgroups (one per CU) and V comes in whole 16-byte chunks (V rows, or
+//    V^T with T % 8 == 0), the loads go straight into LDS (buffer_load ...
+//    lds) and each wave has two buffers, so the tile four further along is
+//    in flight while one is computed; the loads are issued from inline
+//    assembly and waited for with explicit vmcnt counts.  Otherwise two
+//    workgroups share a CU and each wave holds the next tile in registers
+//    while computing the current one.
 //  * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_f16 (a lane owns one
 //    query and 16 keys, so a row's max and sum are in-lane plus one exchange
 //    with the lane 32 away); K rows are permuted so each lane's 8 keys per
@@ -57,10 +64,13 @@ using sattn_lds::tr_offset;
 constexpr int kD = SATTN_HEAD_DIM;
 constexpr int kWaves = 4;
 constexpr int kXcds = 8;
+constexpr int kCus = 256;  // compute units per MI355X
 constexpr int kTileHalfs = 64 * sattn_lds::kRowHalfs;  // one staged 64 x 64 tile
 constexpr int kBufferWord3 = 0x00020000;               // raw buffer, 32-bit data format
 constexpr int kOutOfRange = 0x7FFFFFF0;                // a buffer offset past every range
 constexpr int kLdsDone = 0xC07F;                       // s_waitcnt lgkmcnt(0) only
+constexpr int kVmcnt16 = 0x4F70;                       // s_waitcnt vmcnt(16) only
+constexpr int kVmcnt0 = 0x0F70;                        // s_waitcnt vmcnt(0) only
 
 __device__ __forceinline__ float16v mfma(half8 a, half8 b, float16v c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -79,14 +89,48 @@ __device__ __forceinline__ int krow(int m) {
 
 __device__ __forceinline__ half8 ld8(const half_t* p) { return *reinterpret_cast<const half8*>(p); }
 
-template <bool VT_VEC, bool VROWS>
-__global__ void __launch_bounds__(64 * kWaves, 2)
+// buffer_load_dwordx4 ... lds: lane l's 16 bytes at byte offset voff of the
+// buffer that rsrc describes land at LDS byte lds + 16 l (lds goes in M0,
+// with one wait state before the load reads it).  Offsets past the buffer's
+// range read zeros.  The compiler does not see these loads: the caller waits
+// for them with s_waitcnt vmcnt.
+__device__ __forceinline__ void lds_load16(const int4v& rsrc, unsigned lds, unsigned voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// A raw buffer descriptor (32-bit data format, no stride) as an SGPR quad.
+__device__ __forceinline__ int4v raw_desc(const void* base, unsigned bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  return int4v{__builtin_amdgcn_readfirstlane((int)(unsigned)a),
+               __builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32) & 0xFFFF),
+               __builtin_amdgcn_readfirstlane((int)bytes), kBufferWord3};
+}
+
+__device__ __forceinline__ unsigned lds_addr(const half_t* p) {
+  return (unsigned)(size_t)(__attribute__((address_space(3))) const half_t*)p;
+}
+
+// a compiler fence after an explicit wait, so no LDS read moves above it
+__device__ __forceinline__ void wait_vm(bool keep16) {
+  if (keep16) __builtin_amdgcn_s_waitcnt(kVmcnt16);
+  else __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  asm volatile("" ::: "memory");
+}
+
+template <bool VT_VEC, bool VROWS, bool DMA>
+__global__ void __launch_bounds__(64 * kWaves, DMA ? 1 : 2)
 sattn_fwd_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
                        const half_t* __restrict__ Vt, half_t* __restrict__ O,
                        float* __restrict__ L, float c, int T, int Hq, int G, int nBlocks) {
-  // wave w's region: its K tile and its V^T (or V-rows) tile; after the key
-  // loop, for w > 0, its partial (O^T, m, l) for the merge
-  __shared__ __attribute__((aligned(16))) half_t region[kWaves][2 * kTileHalfs];
+  // Wave w's region: a K tile and a V^T (or V-rows) tile; with DMA a second
+  // such pair and its 32 Q rows.  After the key loop it holds the wave's
+  // partial (O^T, m, l) for the merge.
+  static_assert(!DMA || VT_VEC || VROWS, "LDS loads need whole 16-byte V chunks");
+  constexpr int kRegionHalfs = DMA ? 4 * kTileHalfs + 32 * sattn_lds::kRowHalfs : 2 * kTileHalfs;
+  __shared__ __attribute__((aligned(16))) half_t lds[kWaves * kRegionHalfs];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -106,16 +150,19 @@ sattn_fwd_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ 
   const int row = 32 * blk + n;
   const int need = min(T - 1, 32 * blk + 31) / 64 + 1;  // key tiles up to the diagonal
 
+  half_t* const region = lds + wave * kRegionHalfs;
   half8 qf[4];
+  if constexpr (!DMA) {
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    qf[kk] = row < T ? ld8(Q + ((size_t)h * T + row) * kD + 16 * kk + 8 * g) : half8{};
+    for (int kk = 0; kk < 4; ++kk)
+      qf[kk] = row < T ? ld8(Q + ((size_t)h * T + row) * kD + 16 * kk + 8 * g) : half8{};
+  }
 
   // Staging: lane l owns 16-byte chunk l + 64 i (i < 8) of each tile: row
   // l/8 + 8i, chunk l%8.  K (and V rows) tiles are 8 KiB contiguous; a V^T
   // tile is 64 rows of 128 bytes, T values apart.
-  half_t* const ktile = region[wave];
-  half_t* const vtile = region[wave] + kTileHalfs;
+  half_t* const ktile = region;
+  half_t* const vtile = region + kTileHalfs;
   const int sr = lane >> 3, sc = lane & 7;
   const half_t* Vh = Vt + (size_t)kv * kD * T;  // V^T of head kv, or (VROWS) its V rows
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -164,30 +211,23 @@ sattn_fwd_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ 
   for (int mh = 0; mh < 2; ++mh)
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi) tOff[mh][hi] = VROWS ? tr_offset(lane, false, mh, hi) : 0;
-  auto vt_operand = [&](int ks, int hf) -> half8 {
-    if constexpr (VROWS)
-      return tr8(vtile + 16 * ks * sattn_lds::kRowHalfs, tOff[hf][0], tOff[hf][1]);
-    else
-      return ld8(vtile + vOff[ks] + 32 * hf * sattn_lds::kRowHalfs);
-  };
-
   float m = -INFINITY, l = 0.0f;
   float16v o0 = {}, o1 = {};
   const int swapAddr = (lane ^ 32) << 2;
-  int kt = wave;
-  if (kt < need) load(kt);
-  while (kt < need) {
-    // this wave's own region: its reads of the previous tile were consumed
-    // by the products, so the stores may overwrite it
-    store();
-    __builtin_amdgcn_s_waitcnt(kLdsDone);
-    const int kn = kt + kWaves;
-    if (kn < need) load(kn);
+  // one tile: S^T, the mask on the diagonal tile, the new maximum, P, the
+  // rescale of l and O, P V
+  auto compute = [&](const half_t* kt_lds, const half_t* vt_lds, int kt) {
+    auto vt_operand = [&](int ks, int hf) -> half8 {
+      if constexpr (VROWS)
+        return tr8(vt_lds + 16 * ks * sattn_lds::kRowHalfs, tOff[hf][0], tOff[hf][1]);
+      else
+        return ld8(vt_lds + vOff[ks] + 32 * hf * sattn_lds::kRowHalfs);
+    };
     float16v s0 = {}, s1 = {};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      s0 = mfma(ld8(ktile + kOff[kk]), qf[kk], s0);
-      s1 = mfma(ld8(ktile + kOff[kk] + 32 * sattn_lds::kRowHalfs), qf[kk], s1);
+      s0 = mfma(ld8(kt_lds + kOff[kk]), qf[kk], s0);
+      s1 = mfma(ld8(kt_lds + kOff[kk] + 32 * sattn_lds::kRowHalfs), qf[kk], s1);
     }
     if (kt == need - 1) {  // the tile crossing the block's diagonal
       const int lim = row - kt * 64 - 8 * g;
@@ -228,7 +268,87 @@ sattn_fwd_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ 
       o0 = mfma(vt_operand(ks, 0), p[ks], o0);
       o1 = mfma(vt_operand(ks, 1), p[ks], o1);
     }
-    kt = kn;
+  };
+
+  int kt = wave;
+  if constexpr (DMA) {
+    // Direct-to-LDS staging.  Piece i (1 KiB) of a tile holds its rows 8i ..
+    // 8i+7, and lane l's 16 bytes land at row 8i + l/8, chunk slot l%8, the
+    // slot of chunk (l%8) ^ swz(row); swz depends on the row only through
+    // (row/2) % 8, here on i % 2.
+    const int pr = lane >> 3;
+    int pc[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) pc[e] = (lane & 7) ^ sattn_lds::swz(8 * e + pr);
+    const int4v kdesc = raw_desc(K + (size_t)kv * T * kD, (unsigned)T * kD * 2);
+    const int4v vdesc = raw_desc(Vh, (unsigned)kD * T * 2);
+    half_t* const kA = region;
+    half_t* const vA = region + kTileHalfs;
+    half_t* const kB = region + 2 * kTileHalfs;
+    half_t* const vB = region + 3 * kTileHalfs;
+    half_t* const qrows = region + 4 * kTileHalfs;
+    // Sixteen loads per tile.  The wave's earlier reads of the buffer have
+    // returned (the products consumed them) before it is refilled.
+    auto issue = [&](half_t* kdst, half_t* vdst, int t) {
+      __builtin_amdgcn_s_waitcnt(kLdsDone);
+      const unsigned key0 = (unsigned)t * 64u;
+      const unsigned kl = lds_addr(kdst), vl = lds_addr(vdst);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const unsigned r = 8u * i + pr, ch = (unsigned)pc[i & 1];
+        const unsigned kByte = ((key0 + r) * kD + ch * 8) * 2;  // rows past T: past the range
+        lds_load16(kdesc, __builtin_amdgcn_readfirstlane(kl + 1024u * i), kByte);
+        unsigned vByte = kByte;  // V rows
+        if (!VROWS)  // V^T: chunks at or past T (T % 8 == 0) take an offset past the range
+          vByte = key0 + ch * 8 < (unsigned)T ? (r * (unsigned)T + key0 + ch * 8) * 2
+                                              : (unsigned)kOutOfRange;
+        lds_load16(vdesc, __builtin_amdgcn_readfirstlane(vl + 1024u * i), vByte);
+      }
+    };
+    // Q rows (four pieces, rows past T read as zeros), then tiles kt and
+    // kt + 4: loads complete in order, so waiting for all but the last
+    // sixteen (or for all, with one tile) covers Q and tile kt.
+    {
+      const int4v qdesc = raw_desc(Q + (size_t)h * T * kD, (unsigned)T * kD * 2);
+      const unsigned ql = lds_addr(qrows);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const unsigned r = 32u * blk + 8u * i + pr;
+        lds_load16(qdesc, __builtin_amdgcn_readfirstlane(ql + 1024u * i),
+                   (r * kD + (unsigned)pc[i & 1] * 8) * 2);
+      }
+    }
+    if (kt < need) issue(kA, vA, kt);
+    if (kt + kWaves < need) issue(kB, vB, kt + kWaves);
+    wait_vm(kt + kWaves < need);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qf[kk] = ld8(qrows + chunk_offset(n, 2 * kk + g));
+    // Tile t computes from one buffer while t + 4 lands in the other; then
+    // t + 8 is loaded into the first.  Before computing t, the sixteen loads
+    // of t + 4 (issued after t's) may stay outstanding.
+    while (kt < need) {
+      wait_vm(kt + kWaves < need);
+      compute(kA, vA, kt);
+      if (kt + 2 * kWaves < need) issue(kA, vA, kt + 2 * kWaves);
+      kt += kWaves;
+      if (kt >= need) break;
+      wait_vm(kt + kWaves < need);
+      compute(kB, vB, kt);
+      if (kt + 2 * kWaves < need) issue(kB, vB, kt + 2 * kWaves);
+      kt += kWaves;
+    }
+  } else {
+    if (kt < need) load(kt);
+    while (kt < need) {
+      // this wave's own region: its reads of the previous tile were consumed
+      // by the products, so the stores may overwrite it
+      store();
+      __builtin_amdgcn_s_waitcnt(kLdsDone);
+      const int kn = kt + kWaves;
+      if (kn < need) load(kn);
+      compute(ktile, vtile, kt);
+      kt = kn;
+    }
   }
 
   // merge the four waves' (m, l, O) of the same 32 rows; l is a partial sum
@@ -240,7 +360,7 @@ sattn_fwd_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ 
   // row).  Accumulator element 4 q + e of lane (n, g) is d = 8 q + 4 g + e
   // (o1: d + 32) of row n.
   constexpr int kPartRow = kD + 4;
-  float* const part = reinterpret_cast<float*>(region[wave]);  // [32][68] O, [64] m, [64] l
+  float* const part = reinterpret_cast<float*>(region);  // [32][68] O, [64] m, [64] l
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const float4v va = {o0[4 * q], o0[4 * q + 1], o0[4 * q + 2], o0[4 * q + 3]};
@@ -252,16 +372,15 @@ sattn_fwd_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ 
   part[32 * kPartRow + 64 + lane] = l;
   __syncthreads();
   const int r = 8 * wave + (lane >> 3), ch = lane & 7;  // row r, columns 8 ch .. 8 ch + 7
-  const float* p0 = reinterpret_cast<const float*>(region[0]);
-  float M = p0[32 * kPartRow + r];
+  float M = reinterpret_cast<const float*>(lds)[32 * kPartRow + r];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w)
-    M = fmaxf(M, reinterpret_cast<const float*>(region[w])[32 * kPartRow + r]);
+    M = fmaxf(M, reinterpret_cast<const float*>(lds + w * kRegionHalfs)[32 * kPartRow + r]);
   float lt = 0.0f;
   float4v ya = {}, yb = {};
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
-    const float* pw = reinterpret_cast<const float*>(region[w]);
+    const float* pw = reinterpret_cast<const float*>(lds + w * kRegionHalfs);
     const float aw = __builtin_amdgcn_exp2f(pw[32 * kPartRow + r] - M);  // 0 for a wave with no tile
     const float4v xa = *reinterpret_cast<const float4v*>(pw + r * kPartRow + 8 * ch);
     const float4v xb = *reinterpret_cast<const float4v*>(pw + r * kPartRow + 8 * ch + 4);
@@ -297,13 +416,22 @@ void sattn_fwd_split_launch(const void* Q, const void* K, const void* Vt, void* 
   const half_t* k = static_cast<const half_t*>(K);
   const half_t* v = static_cast<const half_t*>(Vt);
   half_t* o = static_cast<half_t*>(O);
-  if (vrows)
-    hipLaunchKernelGGL((sattn_fwd_split_kernel<false, true>), grid, dim3(64 * kWaves), 0, stream,
-                       q, k, v, o, L, c, T, Hq, G, nBlocks);
+  // LDS staging (one workgroup per CU) when the grid fits the chip at once
+  // and V comes in whole 16-byte chunks; register staging (two per CU)
+  // otherwise
+  const bool dma = (vrows || T % 8 == 0) && grid.x <= (unsigned)kCus;
+#define SATTN_SPLIT(VT, VR, DM)                                                                \
+  hipLaunchKernelGGL((sattn_fwd_split_kernel<VT, VR, DM>), grid, dim3(64 * kWaves), 0, stream, \
+                     q, k, v, o, L, c, T, Hq, G, nBlocks)
+  if (vrows && dma)
+    SATTN_SPLIT(false, true, true);
+  else if (vrows)
+    SATTN_SPLIT(false, true, false);
+  else if (T % 8 == 0 && dma)
+    SATTN_SPLIT(true, false, true);
   else if (T % 8 == 0)
-    hipLaunchKernelGGL((sattn_fwd_split_kernel<true, false>), grid, dim3(64 * kWaves), 0, stream,
-                       q, k, v, o, L, c, T, Hq, G, nBlocks);
+    SATTN_SPLIT(true, false, false);
   else
-    hipLaunchKernelGGL((sattn_fwd_split_kernel<false, false>), grid, dim3(64 * kWaves), 0, stream,
-                       q, k, v, o, L, c, T, Hq, G, nBlocks);
+    SATTN_SPLIT(false, false, false);
+#undef SATTN_SPLIT
 }

@@ -110,3 +110,26 @@ def test_split_key_long_sequences(sattn, dev, shape):
     note(f"split-key kernel, long sequence T={T} Hq={hq} Hkv={hkv}")
     x = make_inputs(T, hq, hkv, seed=24, qk_std=1.25)
     compare(sattn, dev, x, f"split-key T={T} Hq={hq} Hkv={hkv}")
+
+
+@pytest.mark.parametrize("shape", [(2048, 4, 4), (8008, 1, 1), (1000, 8, 8)])
+def test_split_key_lds_staged(sattn, dev, shape):
+    """Grids of at most one workgroup per CU with whole 16-byte V chunks take
+    the split-key kernel's direct-to-LDS staging (two buffers a wave, the
+    loads' waits counted by hand): waves walk up to 32 tiles, alternating the
+    buffers, with ragged last tiles (T=8008, 1000).  Whole outputs against the
+    oracle, and the V-rows entry bit-identical on the same values."""
+    import torch
+    T, hq, hkv = shape
+    note(f"split-key kernel, LDS-staged T={T} Hq={hq} Hkv={hkv}")
+    x = make_inputs(T, hq, hkv, seed=25, peaked_fraction=0.01)
+    O, L = run(sattn, dev, x)
+    Or, Lr = attention_ref(x.Q, x.K, x.Vt, x.c)
+    assert_close(O, L, Or, Lr, f"LDS-staged split-key T={T} Hq={hq} Hkv={hkv}")
+    q = torch.from_numpy(x.Q).to(dev)
+    k = torch.from_numpy(x.K).to(dev)
+    v = torch.from_numpy(np.ascontiguousarray(x.Vt.transpose(0, 2, 1))).to(dev)
+    O2, L2 = sattn.fwd_vrows(q, k, v, x.c)
+    torch.cuda.synchronize()
+    assert np.array_equal(O2.cpu().numpy().astype(np.float64), O)
+    assert np.array_equal(L2.cpu().numpy().astype(np.float64), L)
