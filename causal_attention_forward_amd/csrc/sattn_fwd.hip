@@ -22,15 +22,17 @@
 //  * A wave owns 32 query rows of one head.  A workgroup is eight waves (one
 //    per CU): GW query heads of one GQA group times 8/GW row slots, so each
 //    K/V tile staged in LDS feeds all of them.  Problems too small to give
-//    every CU such a workgroup go to the split-key kernel instead.  Query rows come in 32-row
-//    blocks; a slot takes block n-1-p (heavy) and then block p (light), so
-//    every workgroup carries the same causal work.
+//    every CU such a workgroup go to the split-key kernel instead.  Query
+//    rows come in 32-row blocks; a slot takes block n-1-p (heavy) and then
+//    block p (light), so every workgroup carries the same causal work.
 //  * Each wave is software-pipelined: step j forms P V of tile j-1 and S of
 //    tile j+1 on the matrix cores while its VALUs turn S of tile j into P.
 //    The step is laid out by hand (scheduling barriers): each of its 16
 //    matrix products reads its LDS operand four products ahead and is
 //    followed by the exponentials of two scores.  Two register sets of S and
-//    of binary16 P alternate between steps, so no copies carry them.
+//    of binary16 P alternate between steps, so no copies carry them.  Odd
+//    steps run at a higher wave priority than even ones, so the two waves
+//    sharing a SIMD alternate between the workgroup's barriers.
 //  * K tile t is read at steps t-1 and t, V^T tile t at step t+1.  Two K and
 //    two V^T tiles are staged per barrier, every other step, into rings of 6
 //    and 5 LDS buffers (101 KiB).
