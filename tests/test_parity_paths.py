@@ -133,3 +133,21 @@ def test_split_key_lds_staged(sattn, dev, shape):
     torch.cuda.synchronize()
     assert np.array_equal(O2.cpu().numpy().astype(np.float64), O)
     assert np.array_equal(L2.cpu().numpy().astype(np.float64), L)
+
+
+@pytest.mark.parametrize("shape", [(1024, 8, 2), (1000, 16, 4)])
+def test_split_key_gqa_replication_bitwise(sattn, dev, shape):
+    """The split-key kernels (LDS-staged at T=1024 Hq=8, register-staged at
+    T=1000 Hq=16): K and V^T repeated per query head give bit-identical O and
+    L."""
+    import torch
+    T, hq, hkv = shape
+    note(f"split-key GQA replication T={T} Hq={hq} Hkv={hkv} vs Hkv={hq}")
+    x = make_inputs(T, hq, hkv, seed=42)
+    q, k, vt = (torch.from_numpy(a).to(dev) for a in (x.Q, x.K, x.Vt))
+    O1, L1 = sattn.fwd(q, k, vt, x.c)
+    G = hq // hkv
+    O2, L2 = sattn.fwd(q, k.repeat_interleave(G, 0).contiguous(),
+                       vt.repeat_interleave(G, 0).contiguous(), x.c)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
