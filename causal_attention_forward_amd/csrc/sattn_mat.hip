@@ -15,10 +15,11 @@
 // through HBM where the streaming forward moves the inputs and outputs only.
 //
 // gfx950 design:
-//  * Scores: one workgroup per 64 x 64 tile on or below the diagonal (tiles
-//    above it are never touched), four waves of 32 x 32, each one
-//    v_mfma_f32_32x32x16_f16 chain over the 64 head-width columns with its
-//    operands straight from global memory (16-byte rows of Q and K).  In the
+//  * Scores: one workgroup per run of up to four 64 x 64 tiles of one tile
+//    row (single tiles for small problems) on or below the diagonal (tiles above it are never touched), four
+//    waves of 32 x 32, each one v_mfma_f32_32x32x16_f16 chain per tile over
+//    the 64 head-width columns with its operands straight from global memory
+//    (16-byte rows of Q, loaded once per run, and of K).  In the
 //    accumulator a lane holds one key column, so the 32 lanes of a row store
 //    128 consecutive bytes.  The stores bypass the caches' allocation
 //    (non-temporal): the plane is written once and read back only by the
@@ -33,9 +34,10 @@
 //  * P V: a workgroup takes 128 query rows of a head (a wave 32 rows x all
 //    64 columns) and stages each 64-key V^T tile and the 128 x 64 tile of P
 //    rows in LDS once for its four waves (coalesced loads; P swizzled so the
-//    operand reads hit every bank once).  Keys past the row (only in the
-//    diagonal tile) are masked in registers, so the planes' memory above the
-//    diagonal is never read into a result.
+//    operand reads hit every bank once), with the next four tiles in flight
+//    in four register sets (two when T % 8 != 0).  Keys past the row (only in the diagonal tile)
+//    are masked in registers, so the planes' memory above the diagonal is
+//    never read into a result.  O leaves through LDS as whole row segments.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -73,60 +75,86 @@ __device__ __forceinline__ int xcd_linear() {
 }
 
 // -------------------------------------------------------------------------
-// 1. scores.  Grid (nt (nt+1) / 2 lower-triangle 64 x 64 tiles, Hq), 256
-// threads: wave w computes the 32 x 32 block (w / 2, w % 2) of its tile.
+// 1. scores.  Grid (chunks of the lower triangle, Hq), 256 threads.  A chunk
+// is up to CH consecutive 64-key tiles of one 64-row tile row (CH = 4 when
+// that still leaves many workgroups, else 1); wave w computes block
+// (w / 2, w % 2) of each of them, with its 32 Q rows loaded once per chunk.
 // -------------------------------------------------------------------------
+
+// Chunks in tile rows 0 .. it-1 (row it has it / CH + 1 of them).
+template <int CH>
+__host__ __device__ inline long long chunks_before(int it) {
+  const long long q = it / CH, r = it % CH;
+  return it + (long long)CH * q * (q - 1) / 2 + q * r;
+}
+
+template <int CH>
 __global__ void __launch_bounds__(256)
 sattn_mat_scores_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
                         float* __restrict__ S, float c, int T, int G) {
   const int lin = xcd_linear();
-  const int tile = lin % gridDim.x, h = lin / gridDim.x, kv = h / G;
-  // tile = it (it + 1) / 2 + jt with 0 <= jt <= it
-  int it = (int)((sqrtf(8.0f * (float)tile + 1.0f) - 1.0f) * 0.5f);
-  while ((it + 1) * (it + 2) / 2 <= tile) ++it;
-  while (it * (it + 1) / 2 > tile) --it;
-  const int jt = tile - it * (it + 1) / 2;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
-  const int i0 = it * 64 + 32 * (wave >> 1), j0 = jt * 64 + 32 * (wave & 1);
-  if (j0 > i0 + 31) return;  // a 32 x 32 block wholly above the diagonal
-  const int ia = i0 + n, jb = j0 + n;
-  float16v acc = {};
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const half8 z = {};
-    const half8 a = ia < T ? ld8(Q + ((size_t)h * T + ia) * kD + 16 * kk + 8 * g) : z;
-    const half8 b = jb < T ? ld8(K + ((size_t)kv * T + jb) * kD + 16 * kk + 8 * g) : z;
-    acc = mfma(a, b, acc);
+  const int chunk = lin % gridDim.x, h = lin / gridDim.x, kv = h / G;
+  // the tile row: the largest it with chunks_before(it) <= chunk
+  int lo = 0, hi = (T + 63) / 64;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (chunks_before<CH>(mid) <= chunk) lo = mid;
+    else hi = mid;
   }
-  // element r of lane (n, g): query i0 + 8(r/4) + 4g + r%4, key jb
-  if (j0 + 31 < i0 && j0 + 32 <= T && (T & 3) == 0 && (reinterpret_cast<uintptr_t>(S) & 15) == 0) {
-    // wholly below the diagonal, all 32 keys inside T: the block goes
-    // through the wave's LDS rows so that each store writes 16 bytes a lane,
-    // eight whole 128-byte rows an instruction
-    __shared__ __attribute__((aligned(16))) float blk[4][32 * 36];
-    float* const bw = blk[wave];
+  const int it = lo;
+  const int jt0 = (chunk - (int)chunks_before<CH>(it)) * CH, jt1 = min(jt0 + CH - 1, it);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
+  const int i0 = it * 64 + 32 * (wave >> 1);
+  const int ia = i0 + n;
+  half8 qa[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) bw[(8 * (r >> 2) + 4 * g + (r & 3)) * 36 + n] = acc[r] * c;
-    // other lanes of this wave read what these wrote: order the LDS accesses
-    // (a wave's LDS operations complete in order, so this emits no wait)
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int rr = lane >> 3, ch = lane & 7;
+  for (int kk = 0; kk < 4; ++kk)
+    qa[kk] = ia < T ? ld8(Q + ((size_t)h * T + ia) * kD + 16 * kk + 8 * g) : half8{};
+  __shared__ __attribute__((aligned(16))) float blk[4][32 * 36];
+  float* const bw = blk[wave];
+  const bool rowsAligned = (T & 3) == 0 && (reinterpret_cast<uintptr_t>(S) & 15) == 0;
+  for (int jt = jt0; jt <= jt1; ++jt) {
+    const int j0 = jt * 64 + 32 * (wave & 1);
+    if (j0 > i0 + 31) continue;  // a 32 x 32 block wholly above the diagonal
+    const int jb = j0 + n;
+    float16v acc = {};
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {  // rows 8p + lane/8, keys 4(lane%8) .. +3
-      const int r = 8 * p + rr;
-      const float4v v = *reinterpret_cast<const float4v*>(bw + r * 36 + 4 * ch);
-      if (i0 + r < T)
-        __builtin_nontemporal_store(
-            v, reinterpret_cast<float4v*>(S + (size_t)h * T * T + (size_t)(i0 + r) * T + j0 + 4 * ch));
+    for (int kk = 0; kk < 4; ++kk) {
+      const half8 b = jb < T ? ld8(K + ((size_t)kv * T + jb) * kD + 16 * kk + 8 * g) : half8{};
+      acc = mfma(qa[kk], b, acc);
     }
-  } else if (jb < T) {
-    float* col = S + (size_t)h * T * T + jb;
+    // element r of lane (n, g): query i0 + 8(r/4) + 4g + r%4, key jb
+    if (j0 + 31 < i0 && j0 + 32 <= T && rowsAligned) {
+      // wholly below the diagonal, all 32 keys inside T: the block goes
+      // through the wave's LDS rows so that each store writes 16 bytes a
+      // lane, eight whole 128-byte rows an instruction
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = i0 + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (i < T && jb <= i) __builtin_nontemporal_store(acc[r] * c, col + (size_t)i * T);
+      for (int r = 0; r < 16; ++r) bw[(8 * (r >> 2) + 4 * g + (r & 3)) * 36 + n] = acc[r] * c;
+      // other lanes of this wave read what these wrote, and the next block
+      // overwrites what they read: order the LDS accesses (a wave's LDS
+      // operations complete in order, so this emits no wait)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int rr = lane >> 3, ch = lane & 7;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {  // rows 8p + lane/8, keys 4(lane%8) .. +3
+        const int r = 8 * p + rr;
+        const float4v v = *reinterpret_cast<const float4v*>(bw + r * 36 + 4 * ch);
+        if (i0 + r < T)
+          __builtin_nontemporal_store(
+              v, reinterpret_cast<float4v*>(S + (size_t)h * T * T + (size_t)(i0 + r) * T + j0 + 4 * ch));
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else if (jb < T) {
+      float* col = S + (size_t)h * T * T + jb;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (i < T && jb <= i) __builtin_nontemporal_store(acc[r] * c, col + (size_t)i * T);
+      }
     }
   }
 }
@@ -238,6 +266,8 @@ sattn_mat_softmax_kernel(const float* __restrict__ S, half_t* __restrict__ P,
 // plane's memory above the diagonal is never read into a result.
 // -------------------------------------------------------------------------
 constexpr int kRowHalfs = kD + 8;  // V^T tile row in LDS: 64 keys + 16 bytes of padding
+constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format
+constexpr unsigned kOutOfRange = 0x7FFFFFF0u;  // a buffer offset past every range
 constexpr int kTileHalfs = kD * kRowHalfs;
 constexpr int kPTileHalfs = 128 * sattn_lds::kRowHalfs;  // P tile: 128 rows x 64 keys, swizzled
 
@@ -262,15 +292,38 @@ sattn_mat_pv_kernel(const half_t* __restrict__ P, const half_t* __restrict__ Vt,
   // (row c / 8 of the block, keys 8 (c % 8) ..); rows past T, and keys past T
   // of a row, read as zeros
   const int cr = tid >> 3, cc = tid & 7;
-  half8 st[2], sp[4];
-  auto load = [&](int kt) {
+  // With T % 8 == 0 the loads are buffer loads over the head's V^T and over
+  // the workgroup's rows of P: a chunk lies wholly before or past T, rows past
+  // T fall past the descriptor's range, and chunks past T take an offset past
+  // it, so all read zeros without a branch (and the waits for one register
+  // set leave the other in flight).
+  const unsigned pRows = (unsigned)min(128, T - row0);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<half_t*>(Vh), 0, kD * T * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t prsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<half_t*>(Ph + (size_t)row0 * T), 0, (int)(pRows * (unsigned)T * 2u), kBufferWord3);
+  auto load = [&](int kt, half8 (&st)[2], half8 (&sp)[4]) {
     const int key = kt * 64 + cc * 8;
+    if constexpr (VEC) {
+      // offsets stay below 2^28, so or-ing in kOutOfRange moves a chunk past T
+      // out of range
+      const unsigned oor = key < T ? 0u : kOutOfRange;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const unsigned off = (((unsigned)(cr + 32 * p) * (unsigned)T + (unsigned)key) * 2u) | oor;
+        st[p] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off, 0, 0));
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const unsigned off = (((unsigned)(cr + 32 * p) * (unsigned)T + (unsigned)key) * 2u) | oor;
+        sp[p] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(prsrc, off, 0, 0));
+      }
+      return;
+    }
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int d = cr + 32 * p;
-      if (VEC && key + 7 < T) {
-        st[p] = ld8(Vh + (size_t)d * T + key);
-      } else {
+      {
 #pragma unroll
         for (int e = 0; e < 8; ++e) st[p][e] = key + e < T ? Vh[(size_t)d * T + key + e] : (half_t)0;
       }
@@ -279,15 +332,13 @@ sattn_mat_pv_kernel(const half_t* __restrict__ P, const half_t* __restrict__ Vt,
     for (int p = 0; p < 4; ++p) {
       const int r = row0 + cr + 32 * p;
       const half_t* src = Ph + (size_t)min(r, T - 1) * T + key;
-      if (VEC && r < T && key + 7 < T) {
-        sp[p] = ld8(src);
-      } else {
+      {
 #pragma unroll
         for (int e = 0; e < 8; ++e) sp[p][e] = (r < T && key + e < T) ? src[e] : (half_t)0;
       }
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, const half8 (&st)[2], const half8 (&sp)[4]) {
 #pragma unroll
     for (int p = 0; p < 2; ++p)
       *reinterpret_cast<half8*>(vbuf + buf * kTileHalfs + (cr + 32 * p) * kRowHalfs + cc * 8) = st[p];
@@ -296,12 +347,7 @@ sattn_mat_pv_kernel(const half_t* __restrict__ P, const half_t* __restrict__ Vt,
       *reinterpret_cast<half8*>(pbuf + buf * kPTileHalfs + sattn_lds::chunk_offset(cr + 32 * p, cc)) = sp[p];
   };
   float16v acc0 = {}, acc1 = {};
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) load(kt + 1);
+  auto compute = [&](int kt, int buf) {
     if (kt * 64 <= i0 + 31 && i0 < T) {
       half8 a[4];
       const half_t* pb = pbuf + buf * kPTileHalfs;
@@ -322,19 +368,53 @@ sattn_mat_pv_kernel(const half_t* __restrict__ P, const half_t* __restrict__ Vt,
         acc1 = mfma(a[u], ld8(vb + 32 * kRowHalfs + 16 * u), acc1);
       }
     }
-    if (kt + 1 < nkt) store(buf ^ 1);
-    __syncthreads();
+  };
+  // kSets tiles in flight: tile t is computed from LDS buffer t % 2 while
+  // tiles t + 1 .. t + kSets wait or load in register set (t + i) % kSets.
+  // The steps come in whole groups of kSets and every step issues the same
+  // loads, stores and barrier (past the last tile they repeat it, unused), so
+  // the wait for the oldest set leaves the newer ones in flight.
+  constexpr int kSets = VEC ? 4 : 2;  // the element-wise loads of T % 8 != 0 need more registers
+  half8 st[kSets][2], sp[kSets][4];
+#pragma unroll
+  for (int u = 0; u < kSets; ++u) load(min(u, nkt - 1), st[u], sp[u]);
+  store(0, st[0], sp[0]);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; kt += kSets) {
+#pragma unroll
+    for (int u = 0; u < kSets; ++u) {
+      const int t = kt + u;
+      load(min(t + kSets, nkt - 1), st[u], sp[u]);
+      if (t < nkt) compute(t, u & 1);
+      store((u + 1) & 1, st[(u + 1) % kSets], sp[(u + 1) % kSets]);
+      __syncthreads();
+    }
   }
-  // element r of lane (n, g): query i0 + 8(r/4) + 4g + r%4, column n (acc0) or 32 + n (acc1)
+  // Element r of lane (n, g) is query i0 + 8(r/4) + 4g + r%4, column n (acc0)
+  // or 32 + n (acc1).  The wave's 32 rows go through its own LDS rows (the P
+  // buffers are free once every wave has passed the last tile) so that each
+  // store writes a whole 128-byte row segment with eight lanes.
+  __syncthreads();
   if (i0 < T) {
+    half_t* const ob = pbuf + wave * 32 * kRowHalfs;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int i = i0 + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (i < T) {
-        half_t* o = O + (size_t)i * Hq * kD + (size_t)h * kD + n;
-        o[0] = (half_t)acc0[r];
-        o[32] = (half_t)acc1[r];
-      }
+      half_t* const orow = ob + (8 * (r >> 2) + 4 * g + (r & 3)) * kRowHalfs;
+      orow[n] = (half_t)acc0[r];
+      orow[32 + n] = (half_t)acc1[r];
+    }
+    // other lanes of this wave read what these wrote (a wave's LDS operations
+    // complete in order, so this emits no wait)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int rr = lane >> 3, ch = lane & 7;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 8 * q + rr;
+      if (i0 + r < T)
+        *reinterpret_cast<half8*>(O + (size_t)(i0 + r) * Hq * kD + (size_t)h * kD + 8 * ch) =
+            ld8(ob + r * kRowHalfs + 8 * ch);
     }
   }
 }
@@ -363,10 +443,17 @@ namespace {
 
 void launch_scores(const half_t* q, const half_t* k, float* S, float c, int T, int Hq, int Hkv,
                    hipStream_t strm) {
+  // runs of four tiles per workgroup while that leaves at least 16 per CU
   const int nt = (T + 63) / 64;
-  const unsigned tiles = (unsigned)nt * (unsigned)(nt + 1) / 2u;
-  hipLaunchKernelGGL(sattn_mat_scores_kernel, dim3(tiles, (unsigned)Hq), dim3(256), 0, strm, q,
-                     k, S, c, T, Hq / Hkv);
+  if (chunks_before<4>(nt) * Hq >= 16 * 256) {
+    const unsigned chunks = (unsigned)chunks_before<4>(nt);
+    hipLaunchKernelGGL(sattn_mat_scores_kernel<4>, dim3(chunks, (unsigned)Hq), dim3(256), 0,
+                       strm, q, k, S, c, T, Hq / Hkv);
+  } else {
+    const unsigned chunks = (unsigned)chunks_before<1>(nt);
+    hipLaunchKernelGGL(sattn_mat_scores_kernel<1>, dim3(chunks, (unsigned)Hq), dim3(256), 0,
+                       strm, q, k, S, c, T, Hq / Hkv);
+  }
 }
 
 template <bool VEC>
