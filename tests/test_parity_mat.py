@@ -60,9 +60,13 @@ def check_planes(x, S, P, h, rows):
         assert np.all(Pg[n, i + 1:] == float(SENTINEL_F16)), f"P written above the diagonal, row {i}"
 
 
+# The last two have enough score tiles (at least 16 workgroups per CU) for the
+# scores launch's runs of four tiles per workgroup: one aligned, one with
+# T % 4 != 0 (element-wise stores) and a ragged last tile.
 SHAPES = [(1, 1, 1, {}), (7, 2, 1, {}), (64, 2, 2, {}), (130, 4, 2, {"peaked_fraction": 0.02}),
           (257, 3, 1, {"qk_std": 1.5}), (1000, 16, 4, {"peaked_fraction": 0.01}),
-          (1024, 8, 8, {"qk_std": 0.5, "v_std": 0.5})]
+          (1024, 8, 8, {"qk_std": 0.5, "v_std": 0.5}), (1024, 128, 32, {}),
+          (999, 112, 8, {"peaked_fraction": 0.01})]
 
 
 @pytest.mark.parametrize("T,Hq,Hkv,kw", SHAPES, ids=[f"T{t}_Hq{a}_Hkv{b}" for t, a, b, _ in SHAPES])
