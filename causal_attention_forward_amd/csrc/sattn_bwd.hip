@@ -69,6 +69,7 @@ constexpr int kRowHalfs = sattn_lds::kRowHalfs; // LDS row: 64 values, 16-byte c
 constexpr int kTileHalfs = kTile * kRowHalfs;
 constexpr int kBufferWord3 = 0x00020000;        // raw buffer, 32-bit data format
 constexpr int kOutOfRange = 0x7FFFFFF0;         // a buffer offset past every range
+constexpr int kCus = 256;                       // compute units per MI355X
 constexpr int kXcds = 8;                        // accelerator complex dies per MI355X
 
 // Workgroups are dealt to the eight XCDs round-robin by index.  This returns
@@ -581,15 +582,21 @@ __device__ __forceinline__ void sum_rows_out(const Region& region, float* out, i
   }
 }
 
-template <bool VT_VEC, bool PREFETCH>
-__global__ void __launch_bounds__(64 * kSW, 2)
+// DMA (V^T chunks whole 16-byte loads only): each wave double-buffers its
+// tiles in LDS with direct-to-LDS loads, one workgroup per compute unit;
+// otherwise the next tile waits in registers (PREFETCH) or is loaded at the
+// start of its turn, two workgroups per unit.
+template <bool VT_VEC, bool PREFETCH, bool DMA>
+__global__ void __launch_bounds__(64 * kSW, DMA ? 1 : 2)
 sattn_bwdq_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
                         const half_t* __restrict__ Vt, const half_t* __restrict__ O,
                         const half_t* __restrict__ dO, const float* __restrict__ L,
                         float* __restrict__ dQ, float* __restrict__ D, float c, float s, int T,
                         int Hq, int G, int nBlocks) {
-  // wave w's region: its K tile and V^T tile; afterwards (w > 0) its partial dQ
-  __shared__ __attribute__((aligned(16))) half_t region[kSW][2 * kTileHalfs];
+  // wave w's region: its K tile and V^T tile (with DMA two such pairs);
+  // afterwards its partial dQ
+  static_assert(!DMA || VT_VEC, "LDS loads need whole 16-byte V^T chunks");
+  __shared__ __attribute__((aligned(16))) half_t region[kSW][(DMA ? 4 : 2) * kTileHalfs];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -682,15 +689,8 @@ sattn_bwdq_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__
     }
 
   float16v dq0 = {}, dq1 = {};
-  int kt = wave;
-  if (PREFETCH && kt < nkt) load(kt);
-  while (kt < nkt) {
-    // the previous tile's reads were consumed by the products
-    if (!PREFETCH) load(kt);
-    store();
-    __builtin_amdgcn_s_waitcnt(kLdsDone);
-    const int kn = kt + kSW;
-    if (PREFETCH && kn < nkt) load(kn);
+  // One key tile: S^T and dP^T (started at -D), P, dS, then dQ^T.
+  auto tile = [&](const half_t* kb, const half_t* vb, int kt) {
     float16v s0, s1, p0, p1;
   #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -721,7 +721,71 @@ sattn_bwdq_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__
       dq0 = mfma(tr8(kc, ktOff[0][0], ktOff[0][1]), ds[ck], dq0);
       dq1 = mfma(tr8(kc, ktOff[1][0], ktOff[1][1]), ds[ck], dq1);
     }
-    kt = kn;
+  };
+
+  int kt = wave;
+  if constexpr (DMA) {
+    // Pair A and pair B: a K tile and a V^T tile each.  Piece i (1 KiB) of a
+    // tile holds its rows 8i .. 8i+7, lane l's 16 bytes at row 8i + l/8, slot
+    // l%8, which holds chunk (l%8) ^ swz(row) (swz depends on i only through
+    // i % 2).  K rows past T and V^T chunks past T (T % 8 == 0) read as zeros.
+    const int pr = lane >> 3;
+    int pc[2];
+  #pragma unroll
+    for (int e = 0; e < 2; ++e) pc[e] = (lane & 7) ^ sattn_lds::swz(8 * e + pr);
+    const int4v kdesc = sattn_lds::raw_desc(K + (size_t)kv * T * kD, (unsigned)T * kD * 2);
+    const int4v vdesc = sattn_lds::raw_desc(Vh, (unsigned)kD * T * 2);
+    half_t* const kA = region[wave];
+    half_t* const vA = kA + kTileHalfs;
+    half_t* const kB = kA + 2 * kTileHalfs;
+    half_t* const vB = kA + 3 * kTileHalfs;
+    constexpr int kLoads = 16;  // direct-to-LDS loads per pair
+    // The wave's earlier reads of the pair have returned (the products
+    // consumed them) before it is refilled.
+    auto issue = [&](half_t* kd, half_t* vd, int t) {
+      __builtin_amdgcn_s_waitcnt(kLdsDone);
+      const unsigned key0 = (unsigned)t * kTile;
+      const unsigned kl = sattn_lds::lds_addr(kd), vl = sattn_lds::lds_addr(vd);
+  #pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const unsigned r = 8u * i + pr, ch = (unsigned)pc[i & 1];
+        sattn_lds::lds_load16(kdesc, __builtin_amdgcn_readfirstlane(kl + 1024u * i),
+                              ((key0 + r) * kD + ch * 8) * 2);
+        const unsigned vByte = key0 + ch * 8 < (unsigned)T ? (r * (unsigned)T + key0 + ch * 8) * 2
+                                                           : (unsigned)kOutOfRange;
+        sattn_lds::lds_load16(vdesc, __builtin_amdgcn_readfirstlane(vl + 1024u * i), vByte);
+      }
+    };
+    auto wait_pair = [&](bool keepNext) {
+      if (keepNext) __builtin_amdgcn_s_waitcnt(sattn_lds::vmcnt_only(kLoads));
+      else __builtin_amdgcn_s_waitcnt(sattn_lds::vmcnt_only(0));
+      asm volatile("" ::: "memory");
+    };
+    if (kt < nkt) issue(kA, vA, kt);
+    if (kt + kSW < nkt) issue(kB, vB, kt + kSW);
+    while (kt < nkt) {
+      wait_pair(kt + kSW < nkt);
+      tile(kA, vA, kt);
+      if (kt + 2 * kSW < nkt) issue(kA, vA, kt + 2 * kSW);
+      kt += kSW;
+      if (kt >= nkt) break;
+      wait_pair(kt + kSW < nkt);
+      tile(kB, vB, kt);
+      if (kt + 2 * kSW < nkt) issue(kB, vB, kt + 2 * kSW);
+      kt += kSW;
+    }
+  } else {
+    if (PREFETCH && kt < nkt) load(kt);
+    while (kt < nkt) {
+      // the previous tile's reads were consumed by the products
+      if (!PREFETCH) load(kt);
+      store();
+      __builtin_amdgcn_s_waitcnt(kLdsDone);
+      const int kn = kt + kSW;
+      if (PREFETCH && kn < nkt) load(kn);
+      tile(kb, vb, kt);
+      kt = kn;
+    }
   }
 
   // Sum the four partials in wave order: every wave leaves its partial in its
@@ -732,16 +796,21 @@ sattn_bwdq_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__
   sum_rows_out(region, dQ + (size_t)h * T * kD, 32 * blk, T, s, wave, lane);
 }
 
-template <bool PREFETCH>
-__global__ void __launch_bounds__(64 * kSW, 2)
+// DMA: each wave double-buffers its tiles in LDS with direct-to-LDS loads
+// (the tile four further along lands while one is computed), one workgroup
+// per compute unit; otherwise the tile is loaded into registers at the start
+// of its turn (PREFETCH: one turn ahead) and stored, two workgroups per unit.
+template <bool PREFETCH, bool DMA>
+__global__ void __launch_bounds__(64 * kSW, DMA ? 1 : 2)
 sattn_bwdk_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
                         const half_t* __restrict__ Vt, const half_t* __restrict__ dO,
                         const float* __restrict__ L, const float* __restrict__ D,
                         float* __restrict__ dKp, float* __restrict__ dVp, float c, float s, int T,
                         int Hq, int G, int nBlocks) {
-  // wave w's region: its Q tile, dO tile and the tile's L and -D; afterwards
-  // (w > 0) its partial dK^T and dV^T
-  constexpr int kRegion = 2 * kTileHalfs * 2 + 2 * kTile * 4;  // bytes
+  // wave w's region: its Q tile, dO tile and the tile's L and -D (with DMA:
+  // two such sets, and D instead of -D); afterwards its partial dK^T and dV^T
+  constexpr int kSet = 2 * kTileHalfs * 2 + 2 * kTile * 4;  // bytes
+  constexpr int kRegion = DMA ? 2 * kSet : kSet;
   __shared__ __attribute__((aligned(16))) char region[kSW][kRegion];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -776,7 +845,6 @@ sattn_bwdk_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__
   half_t* const qb = reinterpret_cast<half_t*>(region[wave]);
   half_t* const ob = qb + kTileHalfs;
   float* const lt = reinterpret_cast<float*>(ob + kTileHalfs);  // [L][64], then [-D][64]
-  const float* const dt = lt + kTile;
   const int sr = lane >> 3, sc = lane & 7;
   const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<half_t*>(Q + (size_t)h * T * kD), 0, T * kD * 2, kBufferWord3);
@@ -818,14 +886,12 @@ sattn_bwdk_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__
     for (int hi = 0; hi < 2; ++hi) tOff[mh][hi] = tr_offset(lane, false, mh, hi);
 
   float16v dk0 = {}, dk1 = {}, dv0 = {}, dv1 = {};
-  int it = ft + wave;
-  if (PREFETCH && it < nt) load(it);
-  while (it < nt) {
-    if (!PREFETCH) load(it);
-    store();
-    __builtin_amdgcn_s_waitcnt(kLdsDone);
-    const int in = it + kSW;
-    if (PREFETCH && in < nt) load(in);
+  // One query tile: S, dP (started at -D), P and dS, then dV^T and dK^T.
+  // With DMA the set holds D (negated here) and, for queries past T, L = 0:
+  // their Q and dO rows are zeros, so P = 1 there meets dP - D = 0 and a zero
+  // dO row, and adds nothing.
+  auto tile = [&](const half_t* qb, const half_t* ob, const float* lt, int it) {
+    const float* const dt = lt + kTile;
     float16v nd0, nd1;
   #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -834,8 +900,8 @@ sattn_bwdk_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__
   #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float16v& nd = b < 2 ? nd0 : nd1;
-        nd[8 * (b & 1) + e] = d0[e];
-        nd[8 * (b & 1) + 4 + e] = d1[e];
+        nd[8 * (b & 1) + e] = DMA ? -d0[e] : d0[e];
+        nd[8 * (b & 1) + 4 + e] = DMA ? -d1[e] : d1[e];
       }
     }
     float16v s0, s1, p0, p1;
@@ -881,7 +947,75 @@ sattn_bwdk_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__
       dk0 = mfma(tr8(qc, tOff[0][0], tOff[0][1]), db[ck], dk0);
       dk1 = mfma(tr8(qc, tOff[1][0], tOff[1][1]), db[ck], dk1);
     }
-    it = in;
+  };
+
+  int it = ft + wave;
+  if constexpr (DMA) {
+    // Set A and set B: Q tile, dO tile, L, D.  Piece i (1 KiB) of a tile
+    // holds its rows 8i .. 8i+7, lane l's 16 bytes at row 8i + l/8, slot
+    // l%8, which holds chunk (l%8) ^ swz(row) (swz depends on i only through
+    // i % 2); L and D are one dword a lane.  Rows past T read as zeros.
+    const int pr = lane >> 3;
+    int pc[2];
+  #pragma unroll
+    for (int e = 0; e < 2; ++e) pc[e] = (lane & 7) ^ sattn_lds::swz(8 * e + pr);
+    const int4v qdesc = sattn_lds::raw_desc(Q + (size_t)h * T * kD, (unsigned)T * kD * 2);
+    const int4v odesc = sattn_lds::raw_desc(dO + (size_t)h * kD, (unsigned)(T * Hq - h) * kD * 2);
+    const int4v ldesc = sattn_lds::raw_desc(L + (size_t)h * T, (unsigned)T * 4);
+    const int4v ddesc = sattn_lds::raw_desc(D + (size_t)h * T, (unsigned)T * 4);
+    char* const setA = region[wave];
+    char* const setB = region[wave] + kSet;
+    constexpr int kLoads = 18;  // direct-to-LDS loads per set
+    // The wave's earlier reads of the set have returned (the products
+    // consumed them) before it is refilled.
+    auto issue = [&](char* set, int t) {
+      __builtin_amdgcn_s_waitcnt(kLdsDone);
+      const unsigned q0 = (unsigned)t * kTile;
+      const unsigned ql = sattn_lds::lds_addr(set), ol = ql + kTileHalfs * 2;
+  #pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const unsigned r = q0 + 8u * i + pr, ch = (unsigned)pc[i & 1];
+        sattn_lds::lds_load16(qdesc, __builtin_amdgcn_readfirstlane(ql + 1024u * i), (r * kD + ch * 8) * 2);
+        sattn_lds::lds_load16(odesc, __builtin_amdgcn_readfirstlane(ol + 1024u * i),
+                              (r * (unsigned)Hq * kD + ch * 8) * 2);
+      }
+      const unsigned ll = ol + kTileHalfs * 2;
+      sattn_lds::lds_load4(ldesc, __builtin_amdgcn_readfirstlane(ll), (q0 + lane) * 4);
+      sattn_lds::lds_load4(ddesc, __builtin_amdgcn_readfirstlane(ll + kTile * 4), (q0 + lane) * 4);
+    };
+    auto wait_set = [&](bool keepNext) {
+      if (keepNext) __builtin_amdgcn_s_waitcnt(sattn_lds::vmcnt_only(kLoads));
+      else __builtin_amdgcn_s_waitcnt(sattn_lds::vmcnt_only(0));
+      asm volatile("" ::: "memory");
+    };
+    auto run = [&](const char* set, int t) {
+      const half_t* q = reinterpret_cast<const half_t*>(set);
+      tile(q, q + kTileHalfs, reinterpret_cast<const float*>(q + 2 * kTileHalfs), t);
+    };
+    if (it < nt) issue(setA, it);
+    if (it + kSW < nt) issue(setB, it + kSW);
+    while (it < nt) {
+      wait_set(it + kSW < nt);
+      run(setA, it);
+      if (it + 2 * kSW < nt) issue(setA, it + 2 * kSW);
+      it += kSW;
+      if (it >= nt) break;
+      wait_set(it + kSW < nt);
+      run(setB, it);
+      if (it + 2 * kSW < nt) issue(setB, it + 2 * kSW);
+      it += kSW;
+    }
+  } else {
+    if (PREFETCH && it < nt) load(it);
+    while (it < nt) {
+      if (!PREFETCH) load(it);
+      store();
+      __builtin_amdgcn_s_waitcnt(kLdsDone);
+      const int in = it + kSW;
+      if (PREFETCH && in < nt) load(in);
+      tile(qb, ob, lt, it);
+      it = in;
+    }
   }
 
   // Sum the four partials in wave order: every wave leaves its dK^T partial
@@ -985,7 +1119,11 @@ void launch_query(const half_t* Q, const half_t* K, const half_t* Vt, const half
   const int G = Hq / Hkv;
   const bool vec = T % 8 == 0;
   if (sh.split) {
-    auto sk = vec ? sattn_bwdq_split_kernel<true, true> : sattn_bwdq_split_kernel<false, false>;
+    // direct-to-LDS double buffering (one workgroup per CU) when the grid fits
+    // the chip at once and V^T comes in whole 16-byte chunks
+    auto sk = !vec                        ? sattn_bwdq_split_kernel<false, false, false>
+              : grid.x <= (unsigned)kCus ? sattn_bwdq_split_kernel<true, false, true>
+                                         : sattn_bwdq_split_kernel<true, true, false>;
     hipLaunchKernelGGL(sk, grid, dim3(64 * kSW), 0, stream, Q, K, Vt, O, dO, L, dQ, D, c, s, T, Hq,
                        G, sh.nBlocks);
     return;
@@ -1008,8 +1146,12 @@ void launch_key(const half_t* Q, const half_t* K, const half_t* Vt, const half_t
   const Shape sh = launch_shape(T, Hq);
   const dim3 grid((unsigned)sh.nPairs * (unsigned)Hq);
   if (sh.split) {
-    hipLaunchKernelGGL(sattn_bwdk_split_kernel<false>, grid, dim3(64 * kSW), 0, stream, Q, K, Vt, dO, L, D,
-                       kp, vp, c, s, T, Hq, G, sh.nBlocks);
+    // direct-to-LDS double buffering (one workgroup per CU) when the grid fits
+    // the chip at once
+    auto sk = grid.x <= (unsigned)kCus ? sattn_bwdk_split_kernel<false, true>
+                                       : sattn_bwdk_split_kernel<false, false>;
+    hipLaunchKernelGGL(sk, grid, dim3(64 * kSW), 0, stream, Q, K, Vt, dO, L, D, kp, vp, c, s, T,
+                       Hq, G, sh.nBlocks);
   } else {
     auto kernel = sattn_bwdk_kernel<8, true, true>;
     if (sh.nw == 4) kernel = sh.paired ? sattn_bwdk_kernel<4, true, true> : sattn_bwdk_kernel<4, true, false>;

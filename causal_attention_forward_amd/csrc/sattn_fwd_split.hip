@@ -58,6 +58,9 @@ typedef float float16v __attribute__((ext_vector_type(16)));
 typedef int int4v __attribute__((ext_vector_type(4)));
 
 using sattn_lds::chunk_offset;
+using sattn_lds::lds_addr;
+using sattn_lds::lds_load16;
+using sattn_lds::raw_desc;
 using sattn_lds::tr8;
 using sattn_lds::tr_offset;
 
@@ -69,8 +72,8 @@ constexpr int kTileHalfs = 64 * sattn_lds::kRowHalfs;  // one staged 64 x 64 til
 constexpr int kBufferWord3 = 0x00020000;               // raw buffer, 32-bit data format
 constexpr int kOutOfRange = 0x7FFFFFF0;                // a buffer offset past every range
 constexpr int kLdsDone = 0xC07F;                       // s_waitcnt lgkmcnt(0) only
-constexpr int kVmcnt16 = 0x4F70;                       // s_waitcnt vmcnt(16) only
-constexpr int kVmcnt0 = 0x0F70;                        // s_waitcnt vmcnt(0) only
+constexpr int kVmcnt16 = sattn_lds::vmcnt_only(16);   // s_waitcnt vmcnt(16) only
+constexpr int kVmcnt0 = sattn_lds::vmcnt_only(0);     // s_waitcnt vmcnt(0) only
 
 __device__ __forceinline__ float16v mfma(half8 a, half8 b, float16v c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -88,30 +91,6 @@ __device__ __forceinline__ int krow(int m) {
 }
 
 __device__ __forceinline__ half8 ld8(const half_t* p) { return *reinterpret_cast<const half8*>(p); }
-
-// buffer_load_dwordx4 ... lds: lane l's 16 bytes at byte offset voff of the
-// buffer that rsrc describes land at LDS byte lds + 16 l (lds goes in M0,
-// with one wait state before the load reads it).  Offsets past the buffer's
-// range read zeros.  The compiler does not see these loads: the caller waits
-// for them with s_waitcnt vmcnt.
-__device__ __forceinline__ void lds_load16(const int4v& rsrc, unsigned lds, unsigned voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
-}
-
-// A raw buffer descriptor (32-bit data format, no stride) as an SGPR quad.
-__device__ __forceinline__ int4v raw_desc(const void* base, unsigned bytes) {
-  const unsigned long long a = (unsigned long long)base;
-  return int4v{__builtin_amdgcn_readfirstlane((int)(unsigned)a),
-               __builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32) & 0xFFFF),
-               __builtin_amdgcn_readfirstlane((int)bytes), kBufferWord3};
-}
-
-__device__ __forceinline__ unsigned lds_addr(const half_t* p) {
-  return (unsigned)(size_t)(__attribute__((address_space(3))) const half_t*)p;
-}
 
 // a compiler fence after an explicit wait, so no LDS read moves above it
 __device__ __forceinline__ void wait_vm(bool keep16) {

@@ -1,6 +1,7 @@
 // LDS layout of the 64 x 64 binary16 tiles staged unpadded by the backward
-// and the split-key forward, and the gfx950 transpose read that turns such a
-// tile into a matrix-core operand of its transpose.
+// and the split-key forward, the gfx950 transpose read that turns such a
+// tile into a matrix-core operand of its transpose, and the direct-to-LDS
+// loads that stage them.
 #ifndef SATTN_LDS_H
 #define SATTN_LDS_H
 
@@ -59,6 +60,43 @@ __device__ __forceinline__ int tr_offset(int lane, bool permuted, int mh, int hi
   const int col = 32 * mh + 16 * ((lane >> 4) & 1) + 4 * cb;
   return chunk_offset(row, col >> 3) + (col & 7);
 }
+
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+// Direct-to-LDS loads (buffer_load ... lds): lane l's 16 (or 4) bytes at byte
+// offset voff of the buffer that rsrc describes land at LDS byte
+// lds + 16 l (or 4 l); lds goes in M0, with one wait state before the load
+// reads it.  Offsets past the buffer's range read zeros.  The compiler does
+// not see these loads: callers wait for them with s_waitcnt vmcnt.
+__device__ __forceinline__ void lds_load16(const int4v& rsrc, unsigned lds, unsigned voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_load4(const int4v& rsrc, unsigned lds, unsigned voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// A raw buffer descriptor (32-bit data format, no stride) as an SGPR quad.
+__device__ __forceinline__ int4v raw_desc(const void* base, unsigned bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  return int4v{__builtin_amdgcn_readfirstlane((int)(unsigned)a),
+               __builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32) & 0xFFFF),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
+// The LDS byte address of p.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)(__attribute__((address_space(3))) const char*)p;
+}
+
+// The s_waitcnt operand that waits until at most n vector memory operations
+// are outstanding and for nothing else.
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 }  // namespace sattn_lds
 

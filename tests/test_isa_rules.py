@@ -85,7 +85,7 @@ def test_lds_loads_set_m0_first(code_objects):
     lines = [l.strip() for l in asm.splitlines()]
     hits = 0
     for i, l in enumerate(lines):
-        if re.match(r"buffer_load_dwordx4 .* lds\b", l):
+        if re.match(r"buffer_load_dword\w* .* lds\b", l):
             hits += 1
             assert lines[i - 1].startswith("s_nop"), lines[i - 2:i + 1]
             assert lines[i - 2].startswith("s_mov_b32 m0,"), lines[i - 2:i + 1]
