@@ -29,6 +29,9 @@ FULL = [
     (257, 2, 2, 57, {"qk_std": 1.5}),
     (1000, 16, 4, 2, {"peaked_fraction": 0.01}),
     (1024, 8, 8, 1, {"qk_std": 0.5, "v_std": 0.5}),
+    # a split grid that fits the chip at once (LDS-staged tiles on both sides)
+    # with a ragged last tile and groups of four
+    (1000, 8, 2, 58, {"peaked_fraction": 0.01}),
     # grids large enough for heavy/light block pairing: four-wave workgroups
     # with an odd block count (the middle block pairs with itself) and a
     # non-multiple-of-8 tail, and with an even count; eight-wave workgroups
