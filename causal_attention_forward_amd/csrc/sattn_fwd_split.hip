@@ -9,8 +9,13 @@
 // O folded by the merge rule for normalised weighted sums (a new maximum m'
 // scales l and O by 2^(m - m')), P = 2^(t - m') rounded to binary16 for its
 // product with V, sums in binary32; the epilogue writes O / l (binary16,
-// token-major) and m + log2 l.  Here every tile moves the maximum, as the
-// page's tile body does.
+// token-major) and m + log2 l.  Where V^T can be staged through LDS
+// (T % 8 == 0 and the grid fits the chip at once) the reference is moved
+// lazily, as in the eight-wave kernel: each wave takes its first tile's exact
+// maximum and keeps it while every partial row sum stays within (0, 2^8]
+// (the merge rule holds for any reference, so this changes only rounding);
+// elsewhere every tile moves it, as the page's tile body does.  The V^T and
+// V-rows entries make the same choice, so they give the same bits.
 //
 // gfx950 design:
 //  * Workgroup = four waves on one 32-row query block of one head; wave w
@@ -99,7 +104,7 @@ __device__ __forceinline__ void wait_vm(bool keep16) {
   asm volatile("" ::: "memory");
 }
 
-template <bool VT_VEC, bool VROWS, bool DMA>
+template <bool VT_VEC, bool VROWS, bool DMA, bool LAZY>
 __global__ void __launch_bounds__(64 * kWaves, DMA ? 1 : 2)
 sattn_fwd_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
                        const half_t* __restrict__ Vt, half_t* __restrict__ O,
@@ -108,6 +113,7 @@ sattn_fwd_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ 
   // such pair and its 32 Q rows.  After the key loop it holds the wave's
   // partial (O^T, m, l) for the merge.
   static_assert(!DMA || VT_VEC || VROWS, "LDS loads need whole 16-byte V chunks");
+  static_assert(!LAZY || DMA, "the lazy reference's slow path needs the registers LDS staging frees");
   constexpr int kRegionHalfs = DMA ? 4 * kTileHalfs + 32 * sattn_lds::kRowHalfs : 2 * kTileHalfs;
   __shared__ __attribute__((aligned(16))) half_t lds[kWaves * kRegionHalfs];
 
@@ -196,44 +202,87 @@ sattn_fwd_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ 
   // one tile: S^T, the mask on the diagonal tile, the new maximum, P, the
   // rescale of l and O, P V
   auto compute = [&](const half_t* kt_lds, const half_t* vt_lds, int kt) {
+    const bool first = kt == wave;  // the wave's first tile
     auto vt_operand = [&](int ks, int hf) -> half8 {
       if constexpr (VROWS)
         return tr8(vt_lds + 16 * ks * sattn_lds::kRowHalfs, tOff[hf][0], tOff[hf][1]);
       else
         return ld8(vt_lds + vOff[ks] + 32 * hf * sattn_lds::kRowHalfs);
     };
-    float16v s0 = {}, s1 = {};
+    float16v s0, s1;
+    auto scores = [&]() {  // S^T, masked on the tile crossing the block's diagonal
+      s0 = float16v{};
+      s1 = float16v{};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      s0 = mfma(ld8(kt_lds + kOff[kk]), qf[kk], s0);
-      s1 = mfma(ld8(kt_lds + kOff[kk] + 32 * sattn_lds::kRowHalfs), qf[kk], s1);
-    }
-    if (kt == need - 1) {  // the tile crossing the block's diagonal
-      const int lim = row - kt * 64 - 8 * g;
+      for (int kk = 0; kk < 4; ++kk) {
+        s0 = mfma(ld8(kt_lds + kOff[kk]), qf[kk], s0);
+        s1 = mfma(ld8(kt_lds + kOff[kk] + 32 * sattn_lds::kRowHalfs), qf[kk], s1);
+      }
+      if (kt == need - 1) {
+        const int lim = row - kt * 64 - 8 * g;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int k = 16 * (i >> 3) + (i & 7);
+          if (k > lim) s0[i] = -INFINITY;
+          if (k + 32 > lim) s1[i] = -INFINITY;
+        }
+      }
+    };
+    // the reference moved to the tile's maximum (finite: key 64 kt <= row for
+    // every row), l and O rescaled to it
+    auto exact_reference = [&]() {
+      float x = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x = fmaxf(x, fmaxf(s0[i], s1[i]));
+      x = fmaxf(x, xlane(x, swapAddr));
+      const float m_new = fmaxf(m, x * c);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 when m = -inf
+      m = m_new;
+      l *= alpha;
+      o0 *= alpha;
+      o1 *= alpha;
+    };
+    auto exponentials = [&]() -> float {
+      float sum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int k = 16 * (i >> 3) + (i & 7);
-        if (k > lim) s0[i] = -INFINITY;
-        if (k + 32 > lim) s1[i] = -INFINITY;
+        s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c, -m));
+        s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c, -m));
+        sum += s0[i] + s1[i];
+      }
+      return sum;
+    };
+    scores();
+    // Lazy: after the wave's first tile the reference stays put while every
+    // lane's partial row sum stays within (0, 2^8]; otherwise the slow path
+    // moves it (exactly by a power of two, or to the tile's maximum if a P
+    // overflowed).  Eager: every tile moves it.
+    if (first || !LAZY) exact_reference();
+    float lsum = exponentials();
+    if (LAZY && !first && __builtin_amdgcn_ballot_w64(!(lsum <= 256.0f)) != 0) {
+      float x = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x = fmaxf(x, fmaxf(s0[i], s1[i]));
+      const float pmax = fmaxf(x, xlane(x, swapAddr));
+      if (__builtin_amdgcn_ballot_w64(!(pmax < INFINITY)) == 0) {
+        const int e = pmax > 1.0f ? __builtin_amdgcn_frexp_expf(pmax) : 0;
+        const float alpha = __builtin_ldexpf(1.0f, -e);
+        m += (float)e;
+        l *= alpha;
+        o0 *= alpha;
+        o1 *= alpha;
+        s0 *= alpha;
+        s1 *= alpha;
+        lsum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) lsum += s0[i] + s1[i];
+      } else {
+        scores();
+        exact_reference();
+        lsum = exponentials();
       }
     }
-    float x = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x = fmaxf(x, fmaxf(s0[i], s1[i]));
-    x = fmaxf(x, xlane(x, swapAddr));
-    const float m_new = fmaxf(m, x * c);  // finite: key 64 kt <= row for every row
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    m = m_new;
-    float lsum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c, -m));
-      s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c, -m));
-      lsum += s0[i] + s1[i];
-    }
-    l = l * alpha + lsum;
-    o0 *= alpha;
-    o1 *= alpha;
+    l += lsum;
     half8 p[4];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -397,20 +446,25 @@ void sattn_fwd_split_launch(const void* Q, const void* K, const void* Vt, void* 
   half_t* o = static_cast<half_t*>(O);
   // LDS staging (one workgroup per CU) when the grid fits the chip at once
   // and V comes in whole 16-byte chunks; register staging (two per CU)
-  // otherwise
+  // otherwise.  The lazy reference (LDS staging only: register staging has no
+  // room for its slow path) is taken exactly where the V^T entry can stage
+  // through LDS, so both entries round alike at every shape.
   const bool dma = (vrows || T % 8 == 0) && grid.x <= (unsigned)kCus;
-#define SATTN_SPLIT(VT, VR, DM)                                                                \
-  hipLaunchKernelGGL((sattn_fwd_split_kernel<VT, VR, DM>), grid, dim3(64 * kWaves), 0, stream, \
+  const bool lazy = dma && T % 8 == 0;
+#define SATTN_SPLIT(VT, VR, DM, LZ)                                                                \
+  hipLaunchKernelGGL((sattn_fwd_split_kernel<VT, VR, DM, LZ>), grid, dim3(64 * kWaves), 0, stream, \
                      q, k, v, o, L, c, T, Hq, G, nBlocks)
-  if (vrows && dma)
-    SATTN_SPLIT(false, true, true);
+  if (vrows && lazy)
+    SATTN_SPLIT(false, true, true, true);
+  else if (vrows && dma)
+    SATTN_SPLIT(false, true, true, false);
   else if (vrows)
-    SATTN_SPLIT(false, true, false);
-  else if (T % 8 == 0 && dma)
-    SATTN_SPLIT(true, false, true);
+    SATTN_SPLIT(false, true, false, false);
+  else if (lazy)
+    SATTN_SPLIT(true, false, true, true);
   else if (T % 8 == 0)
-    SATTN_SPLIT(true, false, false);
+    SATTN_SPLIT(true, false, false, false);
   else
-    SATTN_SPLIT(false, false, false);
+    SATTN_SPLIT(false, false, false, false);
 #undef SATTN_SPLIT
 }

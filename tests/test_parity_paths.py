@@ -22,8 +22,9 @@ from parity_util import TOL_L, TOL_O, assert_close, note, run, sample_rows
 
 pytestmark = pytest.mark.gpu
 
-# (T, Hq, Hkv): the first takes the split-key kernel, the second the main kernel
-PATH_SHAPES = [(1000, 8, 2), (4096, 32, 8)]
+# (T, Hq, Hkv): the first two take the split-key kernel (LDS-staged, lazy
+# reference), the third the main kernel
+PATH_SHAPES = [(1000, 8, 2), (2048, 4, 4), (4096, 32, 8)]
 
 
 def rising(T, Hq, Hkv, seed):
