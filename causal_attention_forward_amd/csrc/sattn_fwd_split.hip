@@ -108,7 +108,8 @@ template <bool VT_VEC, bool VROWS, bool DMA, bool LAZY>
 __global__ void __launch_bounds__(64 * kWaves, DMA ? 1 : 2)
 sattn_fwd_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ K,
                        const half_t* __restrict__ Vt, half_t* __restrict__ O,
-                       float* __restrict__ L, float c, int T, int Hq, int G, int nBlocks) {
+                       float* __restrict__ L, float c, int T, int Hq, int G, int nBlocks,
+                       int nPairs, int pairsPerXcd) {
   // Wave w's region: a K tile and a V^T (or V-rows) tile; with DMA a second
   // such pair and its 32 Q rows.  After the key loop it holds the wave's
   // partial (O^T, m, l) for the merge.
@@ -123,14 +124,25 @@ sattn_fwd_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__ 
   const int n = lane & 31;
   const int g = lane >> 5;
 
-  // XCD-contiguous order: K/V head first, query blocks heaviest first, then
-  // the group's query heads
-  const int nWg = gridDim.x, b = blockIdx.x;
-  const int lid = (b % kXcds) * (nWg / kXcds) + min(b % kXcds, nWg % kXcds) + b / kXcds;
-  const int kv = lid / (nBlocks * G);
-  const int rem = lid - kv * nBlocks * G;
-  const int blk = nBlocks - 1 - rem / G;
-  const int h = kv * G + rem % G;
+  // Query blocks are paired, heavy n-1-j with light j (every pair carries
+  // about the same causal work), and pairs are numbered K/V head first, then
+  // j, then the group's query heads.  Workgroups are dealt to the XCDs
+  // round-robin; XCD x takes the contiguous run of pairs x*pairsPerXcd ..,
+  // its first pairsPerXcd workgroups their heavy blocks (heaviest first) and
+  // the next pairsPerXcd the light blocks of the same pairs, so the XCDs
+  // carry equal work and, where two workgroups share a CU, a CU's two
+  // workgroups are one pair.  The grid is padded to whole runs; padding and
+  // the missing partner of an odd middle block exit at once.
+  const int xcd = blockIdx.x % kXcds, pos = blockIdx.x / kXcds;
+  const bool light = pos >= pairsPerXcd;
+  const int pair = xcd * pairsPerXcd + (light ? pos - pairsPerXcd : pos);
+  if (pair >= nPairs) return;
+  const int perKv = ((nBlocks + 1) / 2) * G;
+  const int kv = pair / perKv;
+  const int j = (pair - kv * perKv) / G;
+  const int h = kv * G + (pair - kv * perKv) % G;
+  const int blk = light ? j : nBlocks - 1 - j;
+  if (light && j >= nBlocks - 1 - j) return;
 
   const int row = 32 * blk + n;
   const int need = min(T - 1, 32 * blk + 31) / 64 + 1;  // key tiles up to the diagonal
@@ -439,7 +451,12 @@ void sattn_fwd_split_launch(const void* Q, const void* K, const void* Vt, void* 
                             float c, int T, int Hq, int Hkv, bool vrows, hipStream_t stream) {
   const int G = Hq / Hkv;
   const int nBlocks = (T + 31) / 32;
-  const dim3 grid((unsigned)nBlocks * (unsigned)Hq);
+  // pairs of query blocks (heavy n-1-j, light j) over all query heads, and
+  // the grid padded so each XCD takes a whole run of pairs (see the kernel)
+  const int nPairs = (nBlocks + 1) / 2 * Hq;
+  const int pairsPerXcd = (nPairs + kXcds - 1) / kXcds;
+  const dim3 grid((unsigned)pairsPerXcd * 2u * (unsigned)kXcds);
+  const unsigned units = (unsigned)nBlocks * (unsigned)Hq;  // workgroups with work
   const half_t* q = static_cast<const half_t*>(Q);
   const half_t* k = static_cast<const half_t*>(K);
   const half_t* v = static_cast<const half_t*>(Vt);
@@ -449,11 +466,11 @@ void sattn_fwd_split_launch(const void* Q, const void* K, const void* Vt, void* 
   // otherwise.  The lazy reference (LDS staging only: register staging has no
   // room for its slow path) is taken exactly where the V^T entry can stage
   // through LDS, so both entries round alike at every shape.
-  const bool dma = (vrows || T % 8 == 0) && grid.x <= (unsigned)kCus;
+  const bool dma = (vrows || T % 8 == 0) && units <= (unsigned)kCus;
   const bool lazy = dma && T % 8 == 0;
 #define SATTN_SPLIT(VT, VR, DM, LZ)                                                                \
   hipLaunchKernelGGL((sattn_fwd_split_kernel<VT, VR, DM, LZ>), grid, dim3(64 * kWaves), 0, stream, \
-                     q, k, v, o, L, c, T, Hq, G, nBlocks)
+                     q, k, v, o, L, c, T, Hq, G, nBlocks, nPairs, pairsPerXcd)
   if (vrows && lazy)
     SATTN_SPLIT(false, true, true, true);
   else if (vrows && dma)
