@@ -81,6 +81,28 @@ __device__ __forceinline__ int xcd_order() {
   return xcd * (n / kXcds) + min(xcd, n % kXcds) + idx;
 }
 
+// The split launches' order: 32-row blocks are paired, heavy with light (the
+// pair's causal work is about constant), and pairs numbered K/V head first,
+// then the pair index j, then the group's query heads.  XCD x takes the
+// contiguous run of pairs x * pairsPerXcd ..: its first pairsPerXcd
+// workgroups take the pairs' heavy blocks (heaviest first) and the next
+// pairsPerXcd their light blocks, so the XCDs carry equal work and two
+// workgroups sharing a CU form one pair.  Returns false for the grid's
+// padding and for the missing partner of an odd middle block; otherwise sets
+// the K/V head, the query head and j, with `light` telling which member.
+__device__ __forceinline__ bool split_unit(int nBlocks, int G, int nPairs, int pairsPerXcd, int& kv,
+                                           int& h, int& j, bool& light) {
+  const int xcd = blockIdx.x % kXcds, pos = blockIdx.x / kXcds;
+  light = pos >= pairsPerXcd;
+  const int pair = xcd * pairsPerXcd + (light ? pos - pairsPerXcd : pos);
+  if (pair >= nPairs) return false;
+  const int perKv = ((nBlocks + 1) / 2) * G;
+  kv = pair / perKv;
+  j = (pair - kv * perKv) / G;
+  h = kv * G + (pair - kv * perKv) % G;
+  return !(light && j >= nBlocks - 1 - j);
+}
+
 __device__ __forceinline__ float16v mfma(half8 a, half8 b, float16v c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
@@ -592,7 +614,7 @@ sattn_bwdq_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__
                         const half_t* __restrict__ Vt, const half_t* __restrict__ O,
                         const half_t* __restrict__ dO, const float* __restrict__ L,
                         float* __restrict__ dQ, float* __restrict__ D, float c, float s, int T,
-                        int Hq, int G, int nBlocks) {
+                        int Hq, int G, int nBlocks, int nPairs, int pairsPerXcd) {
   // wave w's region: its K tile and V^T tile (with DMA two such pairs);
   // afterwards its partial dQ
   static_assert(!DMA || VT_VEC, "LDS loads need whole 16-byte V^T chunks");
@@ -603,12 +625,11 @@ sattn_bwdq_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__
   const int n = lane & 31;
   const int g = lane >> 5;
 
-  // K/V head first, then query blocks heaviest first, then the group's heads
-  const int lid = xcd_order();
-  const int kv = lid / (nBlocks * G);
-  const int rem = lid - kv * nBlocks * G;
-  const int blk = nBlocks - 1 - rem / G;
-  const int h = kv * G + rem % G;
+  // heavy query block n-1-j, light block j (see split_unit)
+  int kv, h, jp;
+  bool lightUnit;
+  if (!split_unit(nBlocks, G, nPairs, pairsPerXcd, kv, h, jp, lightUnit)) return;
+  const int blk = lightUnit ? jp : nBlocks - 1 - jp;
   const int row0 = 32 * blk;
   const int row = row0 + n;
   const bool live = row < T;
@@ -806,7 +827,7 @@ sattn_bwdk_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__
                         const half_t* __restrict__ Vt, const half_t* __restrict__ dO,
                         const float* __restrict__ L, const float* __restrict__ D,
                         float* __restrict__ dKp, float* __restrict__ dVp, float c, float s, int T,
-                        int Hq, int G, int nBlocks) {
+                        int Hq, int G, int nBlocks, int nPairs, int pairsPerXcd) {
   // wave w's region: its Q tile, dO tile and the tile's L and -D (with DMA:
   // two such sets, and D instead of -D); afterwards its partial dK^T and dV^T
   constexpr int kSet = 2 * kTileHalfs * 2 + 2 * kTile * 4;  // bytes
@@ -818,12 +839,12 @@ sattn_bwdk_split_kernel(const half_t* __restrict__ Q, const half_t* __restrict__
   const int n = lane & 31;
   const int g = lane >> 5;
 
-  // K/V head first, then key blocks heaviest (first) first, then the group's heads
-  const int lid = xcd_order();
-  const int kv = lid / (nBlocks * G);
-  const int rem = lid - kv * nBlocks * G;
-  const int blk = rem / G;
-  const int h = kv * G + rem % G;
+  // heavy key block j (every later query sees it), light block n-1-j (see
+  // split_unit)
+  int kv, h, jp;
+  bool lightUnit;
+  if (!split_unit(nBlocks, G, nPairs, pairsPerXcd, kv, h, jp, lightUnit)) return;
+  const int blk = lightUnit ? nBlocks - 1 - jp : jp;
   const int key0 = 32 * blk;
   const int key = key0 + n;
   const bool live = key < T;
@@ -1111,6 +1132,18 @@ Shape launch_shape(int T, int Hq) {
   return {4, n4, paired ? (n4 + 1) / 2 : n4, paired, false};
 }
 
+// The split launches' grid: heavy/light pairs of 32-row blocks over all
+// query heads, padded so each XCD takes a whole run of pairs (split_unit).
+struct SplitGrid {
+  int nPairs, pairsPerXcd;
+  unsigned grid, units;
+};
+SplitGrid split_grid(int nBlocks, int Hq) {
+  const int nPairs = (nBlocks + 1) / 2 * Hq;
+  const int perXcd = (nPairs + kXcds - 1) / kXcds;
+  return {nPairs, perXcd, (unsigned)perXcd * 2u * (unsigned)kXcds, (unsigned)nBlocks * (unsigned)Hq};
+}
+
 void launch_query(const half_t* Q, const half_t* K, const half_t* Vt, const half_t* O,
                   const half_t* dO, const float* L, float* dQ, float* D, float c, float s, int T,
                   int Hq, int Hkv, hipStream_t stream) {
@@ -1119,13 +1152,14 @@ void launch_query(const half_t* Q, const half_t* K, const half_t* Vt, const half
   const int G = Hq / Hkv;
   const bool vec = T % 8 == 0;
   if (sh.split) {
-    // direct-to-LDS double buffering (one workgroup per CU) when the grid fits
-    // the chip at once and V^T comes in whole 16-byte chunks
+    // direct-to-LDS double buffering (one workgroup per CU) when the blocks
+    // fit the chip at once and V^T comes in whole 16-byte chunks
+    const SplitGrid sg = split_grid(sh.nBlocks, Hq);
     auto sk = !vec                        ? sattn_bwdq_split_kernel<false, false, false>
-              : grid.x <= (unsigned)kCus ? sattn_bwdq_split_kernel<true, false, true>
-                                         : sattn_bwdq_split_kernel<true, true, false>;
-    hipLaunchKernelGGL(sk, grid, dim3(64 * kSW), 0, stream, Q, K, Vt, O, dO, L, dQ, D, c, s, T, Hq,
-                       G, sh.nBlocks);
+              : sg.units <= (unsigned)kCus ? sattn_bwdq_split_kernel<true, false, true>
+                                           : sattn_bwdq_split_kernel<true, true, false>;
+    hipLaunchKernelGGL(sk, dim3(sg.grid), dim3(64 * kSW), 0, stream, Q, K, Vt, O, dO, L, dQ, D, c, s,
+                       T, Hq, G, sh.nBlocks, sg.nPairs, sg.pairsPerXcd);
     return;
   }
   auto kernel = vec ? sattn_bwdq_kernel<8, true, true> : sattn_bwdq_kernel<8, false, true>;
@@ -1146,12 +1180,13 @@ void launch_key(const half_t* Q, const half_t* K, const half_t* Vt, const half_t
   const Shape sh = launch_shape(T, Hq);
   const dim3 grid((unsigned)sh.nPairs * (unsigned)Hq);
   if (sh.split) {
-    // direct-to-LDS double buffering (one workgroup per CU) when the grid fits
-    // the chip at once
-    auto sk = grid.x <= (unsigned)kCus ? sattn_bwdk_split_kernel<false, true>
-                                       : sattn_bwdk_split_kernel<false, false>;
-    hipLaunchKernelGGL(sk, grid, dim3(64 * kSW), 0, stream, Q, K, Vt, dO, L, D, kp, vp, c, s, T,
-                       Hq, G, sh.nBlocks);
+    // direct-to-LDS double buffering (one workgroup per CU) when the blocks
+    // fit the chip at once
+    const SplitGrid sg = split_grid(sh.nBlocks, Hq);
+    auto sk = sg.units <= (unsigned)kCus ? sattn_bwdk_split_kernel<false, true>
+                                         : sattn_bwdk_split_kernel<false, false>;
+    hipLaunchKernelGGL(sk, dim3(sg.grid), dim3(64 * kSW), 0, stream, Q, K, Vt, dO, L, D, kp, vp, c, s,
+                       T, Hq, G, sh.nBlocks, sg.nPairs, sg.pairsPerXcd);
   } else {
     auto kernel = sattn_bwdk_kernel<8, true, true>;
     if (sh.nw == 4) kernel = sh.paired ? sattn_bwdk_kernel<4, true, true> : sattn_bwdk_kernel<4, true, false>;
