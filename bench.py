@@ -41,6 +41,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sattn_fwd_T4096_Hq32_Hkv8
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_sattn_fwd_T4096_Hq32_Hkv8.txt")
 BWD_KERNEL_SRC = os.path.join(ROOT, "causal_attention_forward_amd", "csrc", "sattn_bwd.hip")
 BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sattn_bwd_T4096_Hq32_Hkv8.txt")
+BWD_COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_sattn_bwd_T4096_Hq32_Hkv8.txt")
 
 
 def causal_flops(T, Hq, d=64):
@@ -94,6 +95,22 @@ def measured_utilisation(path=COUNTERS_FILE, src=KERNEL_SRC):
         return {"mfma_busy": float(kv["mfma_busy"]), "valu_active": float(kv["valu_active"]),
                 "mfma_valu_coexec": float(kv["mfma_valu_coexec"]),
                 "wait_any": float(kv["wait_any"]),
+                "source": os.path.relpath(path, ROOT)}
+    except (KeyError, ValueError):
+        return None
+
+
+def measured_utilisation_backward(path=BWD_COUNTERS_FILE, src=BWD_KERNEL_SRC):
+    """The backward key launch's matrix-core and VALU utilisation from the
+    committed rocprofv3 SQ-counter summary (fractions of the SIMD-cycles of a
+    dispatch), or None when missing or taken on a different kernel source."""
+    kv = counter_summary(path, src)
+    if not kv:
+        return None
+    try:
+        return {"mfma_busy": float(kv["key_mfma_busy"]), "valu_active": float(kv["key_valu_active"]),
+                "mfma_valu_coexec": float(kv["key_mfma_valu_coexec"]),
+                "wait_any": float(kv["key_wait_any"]),
                 "source": os.path.relpath(path, ROOT)}
     except (KeyError, ValueError):
         return None
@@ -371,7 +388,9 @@ def bench_backward(args, torch, sattn, x, w):
                      "traffic": (measured_traffic(BWD_TRAFFIC_FILE, BWD_KERNEL_SRC)
                                  if args.workload == WORKLOAD_INDEX else None),
                      "kernel": "key launch + reduction (4 products)",
-                     "kernel_ms": round(key_ms, 5)},
+                     "kernel_ms": round(key_ms, 5),
+                     "counters": (measured_utilisation_backward()
+                                  if args.workload == WORKLOAD_INDEX else None)},
     }
     if not args.no_clock:
         out["clock"] = clock_fields(gfx_clock_window(torch, step), value)

@@ -48,6 +48,12 @@ def test_backward_traffic_summary_matches_the_kernel_source():
     assert 193986560 <= got <= 1.05 * 193986560
 
 
+def test_backward_counter_summary_matches_the_kernel_source():
+    got = bench.measured_utilisation_backward()
+    assert got is not None, "profiles/ backward SQ counter summary is stale or missing"
+    assert 0.0 < got["mfma_busy"] < 1.0 and 0.0 < got["valu_active"] < 1.0
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
