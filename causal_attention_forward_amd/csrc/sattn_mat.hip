@@ -384,9 +384,11 @@ sattn_mat_pv_kernel(const half_t* __restrict__ P, const half_t* __restrict__ Vt,
 #pragma unroll
     for (int u = 0; u < kSets; ++u) {
       const int t = kt + u;
+      // tile t + 1 goes into the buffer tile t - 1 left before the last
+      // barrier, ahead of tile t's products so its stores complete under them
+      store((u + 1) & 1, st[(u + 1) % kSets], sp[(u + 1) % kSets]);
       load(min(t + kSets, nkt - 1), st[u], sp[u]);
       if (t < nkt) compute(t, u & 1);
-      store((u + 1) & 1, st[(u + 1) % kSets], sp[(u + 1) % kSets]);
       __syncthreads();
     }
   }
