@@ -10,7 +10,8 @@ second input set, so the replay must read the live inputs: it is compared with
 an eager call on that second set.  Covered: the eight-wave forward, the
 split-key forward (LDS-staged, register-staged, and T % 8 != 0), V given as
 rows, the backward (split launches with the grouped reduction, and the
-eight-wave launches), and the key launch with the library's static workspace.
+eight-wave launches), the key launch with the library's static workspace, and
+the materialised path's three launches.
 The library allocates nothing and records no memset, so a capture holds only
 its kernels.  One forward replay is also checked against the float64 oracle.
 """
@@ -183,3 +184,61 @@ def test_noalloc_key_launch_graph_replay(sattn, dev):
                                            torch.cuda.current_stream().cuda_stream) == sattn.SATTN_OK
 
     _replays(torch, g, [dK, dVt], [eK, eVt], between, lambda: None, lambda: [eK, eVt])
+
+
+MAT_CASES = [(1000, 16, 4), (257, 6, 2)]
+
+
+@pytest.mark.parametrize("T,Hq,Hkv", MAT_CASES)
+def test_materialised_graph_replay(sattn, dev, T, Hq, Hkv):
+    """sattn_mat_fwd captured (scores, softmax and P.V launches): the planes and
+    O, L of every replay equal the eager call's; the last after new Q and K."""
+    import torch
+    note(f"graph replay materialised T={T} Hq={Hq} Hkv={Hkv}")
+    x = make_inputs(T, Hq, Hkv, seed=77)
+    y = make_inputs(T, Hq, Hkv, seed=78)
+    q, k, vt = (torch.from_numpy(a).to(dev) for a in (x.Q, x.K, x.Vt))
+    O = torch.empty((T, Hq * 64), dtype=torch.float16, device=dev)
+    L = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    S = torch.zeros((Hq, T, T), dtype=torch.float32, device=dev)
+    P = torch.zeros((Hq, T, T), dtype=torch.float16, device=dev)
+    Oe, Le, Se, Pe = (t.clone() for t in sattn.mat_fwd(q, k, vt, x.c, scores=S, probs=P))
+    g = _capture(torch, lambda: sattn.mat_fwd(q, k, vt, x.c, scores=S, probs=P, out=O, lse=L))
+    q2, k2 = (torch.from_numpy(a).to(dev) for a in (y.Q, y.K))
+    jO, jL = torch.empty_like(O), torch.empty_like(L)
+    jS, jP = torch.zeros_like(S), torch.zeros_like(P)
+    tri = torch.tril(torch.ones((T, T), dtype=torch.bool, device=dev))
+
+    def between():
+        sattn.mat_fwd(q2, k2, vt, x.c, scores=jS, probs=jP, out=jO, lse=jL)
+        jO.fill_(0)
+
+    def swap():
+        q.copy_(torch.from_numpy(y.Q))
+        k.copy_(torch.from_numpy(y.K))
+
+    def swapped():
+        S2, P2 = torch.zeros_like(S), torch.zeros_like(P)
+        r = sattn.mat_fwd(torch.from_numpy(y.Q).to(dev), torch.from_numpy(y.K).to(dev), vt, x.c,
+                          scores=S2, probs=P2)
+        return [r[0], r[1]]
+
+    # the planes keep whatever is above the diagonal, so only O and L are NaN-filled
+    # between replays and the planes are compared on and below the diagonal
+    for r in range(3):
+        O.fill_(float("nan"))
+        L.fill_(float("nan"))
+        S.masked_fill_(tri, float("nan"))
+        P.masked_fill_(tri, float("nan"))
+        between()
+        if r == 2:
+            swap()
+            expect = swapped()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        if r < 2:
+            assert torch.equal(O, Oe) and torch.equal(L, Le), f"replay {r} differs from the eager call"
+            assert torch.equal(S[:, tri], Se[:, tri]) and torch.equal(P[:, tri], Pe[:, tri])
+        else:
+            assert torch.equal(O, expect[0]) and torch.equal(L, expect[1])
